@@ -1,0 +1,320 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test names the step it pins.  Kinds: library routines (torch fp64 SDPA,
+torch's bf16/float8 conversions), closed forms (bilinearity of the pooled score,
+alpha = 0 and alpha > 1, single-key rows, equal keys), a hand-worked example, brute
+force with pure-Python loops on tiny inputs, and invariants (forced blocks,
+monotone in alpha, GQA == MHA with repeated K/V).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+RNG = np.random.default_rng(7)
+
+
+def rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------- input decoding
+def test_decode_bf16_matches_torch():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    ours = O.decode_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+
+
+def test_decode_e4m3fn_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+
+
+def test_quantiser_codes_roundtrip_and_saturate():
+    """Generator fp8 codes: per-head max |code| is 448 and code*scale is within half an
+    e4m3 ulp of the source value (checked through torch's own decoder)."""
+    x = (rand(300, 2, 16) * 3).astype(np.float32)
+    for h in range(2):
+        codes, s = synth.quantize_e4m3fn(x[:, h])
+        vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        assert np.max(np.abs(vals)) == 448.0
+        y = x[:, h].astype(np.float64) / float(s)
+        # e4m3 relative spacing 2^-3 for normals, absolute 2^-9 for subnormals
+        tol = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6)
+        assert np.all(np.abs(vals - y) <= tol)
+
+
+# ------------------------------------------------------------- pooling + scoring
+def test_pooled_score_is_mean_of_token_logits():
+    """P1 closed form (bilinearity): scale * mean(q_block) . mean(k_block) equals the
+    mean over the B x B token pairs of scale * q_a . k_b, including a partial tail."""
+    L, hq, hkv, d, B = 37, 4, 2, 16, 8
+    q, k = rand(L, hq, d), rand(L, hkv, d)
+    scale = 1 / math.sqrt(d)
+    s = O.block_scores(O.pool(q, B), O.pool(k, B), scale)
+    nb = -(-L // B)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        for i in range(nb):
+            for j in range(i + 1):
+                ta = range(i * B, min(L, (i + 1) * B))
+                tb = range(j * B, min(L, (j + 1) * B))
+                acc = 0.0
+                for a in ta:
+                    for b in tb:
+                        acc += scale * float(np.dot(q[a, h], k[b, g]))
+                acc /= len(ta) * len(tb)
+                assert s[h, i, j] == pytest.approx(acc, rel=1e-12, abs=1e-13)
+            assert np.all(np.isneginf(s[h, i, i + 1:]))
+
+
+def test_pool_partial_block_divides_by_valid_rows():
+    x = np.zeros((10, 1, 2))
+    x[8:, 0, 0] = [3.0, 5.0]  # block 2 of size 4 has 2 valid rows
+    p = O.pool(x, 4)
+    assert p.shape == (1, 3, 2)
+    assert p[0, 2, 0] == 4.0 and p[0, 0, 0] == 0.0
+
+
+# ----------------------------------------------------------- hand-worked example
+def test_hand_worked_selection():
+    """Three 2-token blocks, d = 2, by hand:
+    qbar = (1,0), (0,2), (1,1); kbar = (1,0), (0,1), (0,0).
+    Row 1 logits (x sqrt 2): [0, 2] -> P = [e^-sqrt2, 1] = [0.2431, 1].
+    Row 2 logits (x sqrt 2): [1, 1, 0] -> P = [1, 1, e^-(1/sqrt2)] = [1, 1, 0.4931]."""
+    q = np.array([[1, 0], [1, 0], [0, 2], [0, 2], [1, 1], [1, 1]], float)[:, None, :]
+    k = np.array([[2, 0], [0, 0], [0, 1], [0, 1], [1, 1], [-1, -1]], float)[:, None, :]
+    r = O.select_blocks(q, k, 2, alpha=0.25, n_sink=0, n_local=1)
+    assert r["P"][0, 1, 0] == pytest.approx(math.exp(-math.sqrt(2)), rel=1e-14)
+    assert r["P"][0, 2, 2] == pytest.approx(math.exp(-1 / math.sqrt(2)), rel=1e-14)
+    assert [list(x) for x in r["lists"][0]] == [[0], [1], [0, 1, 2]]
+    r = O.select_blocks(q, k, 2, alpha=0.24, n_sink=0, n_local=1)
+    assert [list(x) for x in r["lists"][0]] == [[0], [0, 1], [0, 1, 2]]
+    r = O.select_blocks(q, k, 2, alpha=0.5, n_sink=0, n_local=1)
+    assert [list(x) for x in r["lists"][0]] == [[0], [1], [0, 1, 2]]
+    r = O.select_blocks(q, k, 2, alpha=0.9, n_sink=1, n_local=1)
+    assert [list(x) for x in r["lists"][0]] == [[0], [0, 1], [0, 1, 2]]
+    r = O.select_blocks(q, k, 2, alpha=1.01, n_sink=0, n_local=1)
+    assert [list(x) for x in r["lists"][0]] == [[0], [1], [2]]
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_force_lists(q, k, B, alpha, n_sink, n_local):
+    """Independent pure-Python selection from token-level logits (tiny inputs only):
+    block score = mean of scale * q_a . k_b over the token pairs of the two blocks,
+    row max over causal blocks, keep = score/max-ratio test or forced block."""
+    L, hq, d = q.shape
+    g_size = hq // k.shape[1]
+    scale = 1 / math.sqrt(d)
+    nb = -(-L // B)
+    out = []
+    for h in range(hq):
+        rows = []
+        for i in range(nb):
+            sc = []
+            for j in range(i + 1):
+                tot, n = 0.0, 0
+                for a in range(i * B, min(L, (i + 1) * B)):
+                    for b in range(j * B, min(L, (j + 1) * B)):
+                        tot += scale * sum(q[a, h, c] * k[b, h // g_size, c] for c in range(d))
+                        n += 1
+                sc.append(tot / n)
+            m = max(sc)
+            lst = []
+            for j in range(i + 1):
+                ratio = math.exp(sc[j] - m)
+                if ratio >= alpha or j < n_sink or j >= i - n_local + 1:
+                    lst.append(j)
+            rows.append(lst)
+        out.append(rows)
+    return out
+
+
+@pytest.mark.parametrize("alpha,n_sink,n_local", [(0.0, 1, 1), (0.3, 1, 2), (0.7, 0, 1), (1.0, 2, 1), (1.5, 1, 3)])
+def test_selection_matches_brute_force(alpha, n_sink, n_local):
+    L, hq, hkv, d, B = 45, 4, 2, 8, 8
+    rng = np.random.default_rng(11)
+    q, k = rand(L, hq, d, rng=rng), rand(L, hkv, d, rng=rng)
+    r = O.select_blocks(q, k, B, alpha, n_sink, n_local)
+    bf = _brute_force_lists(q, k, B, alpha, n_sink, n_local)
+    for h in range(hq):
+        for i in range(len(bf[h])):
+            assert list(r["lists"][h][i]) == bf[h][i]
+            assert r["counts"][h, i] == len(bf[h][i])
+
+
+# ---------------------------------------------------------------- closed forms
+def _small_workload(seed=3, hq=4, hkv=2, lengths=(1000,), **kw):
+    return synth.make_workload("t", hq, hkv, list(lengths), seed=seed, d=32, block=64, **kw)
+
+
+def _f64(wl):
+    if wl.dtype == "bf16":
+        return O.decode_bf16(wl.q), O.decode_bf16(wl.k), O.decode_bf16(wl.v)
+    return (O.dequantize(wl.q, wl.q_scale), O.dequantize(wl.k, wl.k_scale),
+            O.dequantize(wl.v, wl.v_scale))
+
+
+def test_alpha_zero_is_dense():
+    """P4: alpha = 0 keeps every causal block and sparse attention equals dense."""
+    wl = _small_workload()
+    q, k, v = _f64(wl)
+    r = O.select_blocks(q, k, 64, 0.0, 1, 1)
+    nb = r["counts"].shape[1]
+    assert np.array_equal(r["counts"], np.tile(np.arange(1, nb + 1), (wl.hq, 1)))
+    sp = O.sparse_attention(q, k, v, r["lists"], 64)
+    de = O.dense_attention(q, k, v)
+    assert np.max(np.abs(sp - de)) <= 1e-12
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(1, 4), (2, 1), (0, 3), (5, 2)])
+def test_alpha_above_one_keeps_exactly_forced_blocks(n_sink, n_local):
+    """P5: for alpha > 1 the list is {0..min(n_sink, i+1)-1} U {max(0, i-n_local+1)..i}."""
+    wl = _small_workload()
+    q, k, _ = _f64(wl)
+    r = O.select_blocks(q, k, 64, 1.0 + 1e-9, n_sink, n_local)
+    for h in range(wl.hq):
+        for i, lst in enumerate(r["lists"][h]):
+            want = sorted(set(range(min(n_sink, i + 1))) | set(range(max(0, i - n_local + 1), i + 1)))
+            assert list(lst) == want
+
+
+def test_forced_blocks_argmax_and_monotone_in_alpha():
+    """P3: sink/local blocks always present, the row argmax is kept for alpha <= 1, and
+    kept sets nest as alpha grows; lists are strictly ascending and end at i (P6)."""
+    wl = _small_workload(seed=5, lengths=(2000,))
+    q, k, _ = _f64(wl)
+    prev = None
+    for alpha in [0.0, 0.01, 0.05, 0.1, 0.2, 0.5, 1.0]:
+        r = O.select_blocks(q, k, 64, alpha, 1, 2)
+        keep = r["keep"]
+        nb = keep.shape[1]
+        for h in range(wl.hq):
+            for i in range(nb):
+                lst = r["lists"][h][i]
+                assert np.all(np.diff(lst) > 0) and lst[-1] == i and lst[0] >= 0
+                assert 0 in lst and (i - 1 in lst or i == 0)
+                assert int(np.argmax(r["s"][h, i, :i + 1])) in lst
+        if prev is not None:
+            assert np.all(keep <= prev)
+        prev = keep
+
+
+# ------------------------------------------------------------ attention pins
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch fp64 SDPA on CPU with [L, H, d] inputs (K/V already per query head)."""
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).permute(1, 0, 2)
+    tv = torch.from_numpy(v).permute(1, 0, 2)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, is_causal=causal)
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_dense_matches_torch_sdpa():
+    """P7: library routine, causal SDPA in fp64 on CPU; GQA via repeated K/V."""
+    L, hq, hkv, d = 300, 4, 2, 32
+    q, k, v = rand(L, hq, d), rand(L, hkv, d), rand(L, hkv, d)
+    ours = O.dense_attention(q, k, v)
+    ref = _sdpa(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), causal=True)
+    assert np.max(np.abs(ours - ref)) <= 1e-12
+
+
+def test_sparse_matches_sdpa_with_block_mask():
+    """P8: sparse attention equals SDPA with the explicit token mask
+    [block(c) in list(h, block(t))] and c <= t, built from the lists by brute force."""
+    wl = _small_workload(seed=9, lengths=(700,))
+    q, k, v = _f64(wl)
+    B = 64
+    r = O.select_blocks(q, k, B, 0.3, 1, 1)
+    ours = O.sparse_attention(q, k, v, r["lists"], B)
+    L = q.shape[0]
+    g = wl.hq // wl.hkv
+    for h in range(wl.hq):
+        mask = np.zeros((L, L), dtype=bool)
+        for t in range(L):
+            for c in range(t + 1):
+                mask[t, c] = (c // B) in set(r["lists"][h][t // B].tolist())
+        ref = _sdpa(q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1], mask=mask[None])
+        assert np.max(np.abs(ours[:, h] - ref[:, 0])) <= 1e-12
+    assert r["counts"].sum() < r["keep"].shape[0] * (r["keep"].shape[1] * (r["keep"].shape[1] + 1)) // 2
+
+
+def test_attention_closed_forms():
+    """P9: the first query sees only itself (O = V[0]); with all keys equal the softmax
+    is uniform, so O[t] is the mean of V over the visible keys."""
+    L, d, B = 200, 16, 64
+    q, v = rand(L, 1, d), rand(L, 1, d)
+    k = np.tile(rand(1, 1, d), (L, 1, 1))
+    lists = [[np.array([0]), np.array([1]), np.array([0, 2]), np.array([1, 3])]]
+    o = O.sparse_attention(q, k, v, lists, B)
+    assert np.max(np.abs(o[0, 0] - v[0, 0])) <= 1e-15
+    for t in [0, 5, 63, 64, 100, 130, 150, 199]:
+        i = t // B
+        vis = [c for c in range(t + 1) if c // B in lists[0][i]]
+        assert np.max(np.abs(o[t, 0] - v[vis, 0].mean(axis=0))) <= 1e-12
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    """P10: a GQA run equals an MHA run with K/V repeated per query head."""
+    wl = _small_workload(seed=13, lengths=(640,))
+    q, k, v = _f64(wl)
+    g = wl.hq // wl.hkv
+    r1 = O.select_blocks(q, k, 64, 0.2, 1, 2)
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    r2 = O.select_blocks(q, kr, 64, 0.2, 1, 2)
+    assert np.array_equal(r1["keep"], r2["keep"])
+    o1 = O.sparse_attention(q, k, v, r1["lists"], 64)
+    o2 = O.sparse_attention(q, kr, vr, r2["lists"], 64)
+    assert np.max(np.abs(o1 - o2)) <= 1e-13
+
+
+def test_varlen_dense_matches_block_diagonal_sdpa():
+    """P11 (oracle side): a packed batch equals SDPA over the whole packed sequence
+    with a block-diagonal causal mask (no attention across sequences)."""
+    lengths = [100, 257, 64]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, hq, d = cu[-1], 2, 16
+    q, k, v = rand(T, hq, d), rand(T, hq, d), rand(T, hq, d)
+    ours = O.dense_attention_varlen(q, k, v, cu)
+    seg = np.repeat(np.arange(len(lengths)), lengths)
+    mask = (seg[:, None] == seg[None, :]) & (np.arange(T)[None, :] <= np.arange(T)[:, None])
+    ref = _sdpa(q, k, v, mask=mask[None])
+    assert np.max(np.abs(ours - ref)) <= 1e-12
+
+
+def test_varlen_sparse_rows_are_per_sequence():
+    wl = _small_workload(seed=17, lengths=(300, 129, 64))
+    q, k, v = _f64(wl)
+    cu = wl.cu_seqlens
+    sel = O.select_blocks_varlen(q, k, cu, 64, 0.2, 1, 1)
+    o = O.sparse_attention_varlen(q, k, v, cu, [s["lists"] for s in sel], 64)
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        r = O.select_blocks(q[a:b], k[a:b], 64, 0.2, 1, 1)
+        assert np.array_equal(r["keep"], sel[s]["keep"])
+        assert np.max(np.abs(O.sparse_attention(q[a:b], k[a:b], v[a:b], r["lists"], 64) - o[a:b])) == 0
+
+
+def test_lse_matches_logsumexp():
+    wl = _small_workload(seed=19, lengths=(256,))
+    q, k, v = _f64(wl)
+    r = O.select_blocks(q, k, 64, 0.1, 1, 1)
+    _, lse = O.sparse_attention(q, k, v, r["lists"], 64, want_lse=True)
+    h, t = 3, 200
+    g = h // (wl.hq // wl.hkv)
+    vis = [c for c in range(t + 1) if c // 64 in r["lists"][h][t // 64]]
+    x = (q[t, h] @ k[vis, g].T) / math.sqrt(q.shape[-1])
+    assert lse[h, t] == pytest.approx(float(torch.logsumexp(torch.from_numpy(x), 0)), rel=1e-13)
