@@ -1,0 +1,228 @@
+"""MI355X-native FlashPrefill block-sparse prefill attention.
+
+Thin Python binding over libflashprefill.so (C ABI in include/flashprefill.h).
+Every step of the path runs in the HIP kernels; this module only marshals
+arguments: it takes torch tensors for device memory, passes their data
+pointers, strides and the current HIP stream, and allocates outputs with
+torch.  There is no CPU fallback: if the library is missing, loading fails.
+
+Stages (FlashPrefill, Methods 1-3; FlashPrefill V2 for FP8 and paged KV):
+    discover            -> pooled Q/K block means (fp64)
+    threshold_compact   -> per-(head, query block) ascending key-block lists
+    sparse_attn         -> causal GQA attention over the listed blocks (bf16 out)
+and dense_attn, plus *_paged / *_varlen variants for packed batches.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from ._lib import (FP_BF16, FP_FP8_E4M3, FlashPrefillError, call, load)
+
+__all__ = [
+    "FlashPrefillError", "load", "discover", "threshold_compact", "sparse_attn", "dense_attn", "prefill",
+    "VarlenBatch", "discover_paged", "threshold_compact_varlen", "sparse_attn_paged", "idx_capacity",
+    "BLOCK", "HEAD_DIM",
+]
+
+BLOCK = 128
+HEAD_DIM = 128
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FP_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16, float8_e4m3fn or uint8 e4m3fn codes)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _nb(L: int) -> int:
+    return -(-int(L) // BLOCK)
+
+
+def idx_capacity(hq: int, nb: int) -> int:
+    return hq * nb * (nb + 1) // 2
+
+
+def default_scale(d: int = HEAD_DIM) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+# ------------------------------------------------------------- single sequence
+def discover(q: torch.Tensor, k: torch.Tensor, q_scale=None, k_scale=None, pooled_q=None, pooled_k=None):
+    """Mean-pool Q [L, hq, 128] and K [L, hkv, 128] per 128-token block -> fp64
+    ([hq, nb, 128], [hkv, nb, 128])."""
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    nb = _nb(L)
+    if pooled_q is None:
+        pooled_q = torch.empty((hq, nb, d), dtype=torch.float64, device=q.device)
+    if pooled_k is None:
+        pooled_k = torch.empty((hkv, nb, d), dtype=torch.float64, device=q.device)
+    call("fp_discover", _ptr(q), _ptr(k), _dtype_code(q), _ptr(q_scale), _ptr(k_scale), L, hq, hkv, d, BLOCK,
+         q.stride(0), q.stride(1), k.stride(0), k.stride(1), _ptr(pooled_q), _ptr(pooled_k), _stream(q))
+    return pooled_q, pooled_k
+
+
+def threshold_compact(pooled_q: torch.Tensor, pooled_k: torch.Tensor, alpha: float, n_sink: int, n_local: int,
+                      softmax_scale: Optional[float] = None, idx=None, counts=None):
+    """Block scores, alpha x row-max threshold with sink/local blocks, ascending
+    lists -> (idx int32 triangular-packed [hq * nb(nb+1)/2], counts int32 [hq, nb])."""
+    hq, nb, d = pooled_q.shape
+    hkv = pooled_k.shape[0]
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if idx is None:
+        idx = torch.zeros(idx_capacity(hq, nb), dtype=torch.int32, device=pooled_q.device)
+    if counts is None:
+        counts = torch.empty((hq, nb), dtype=torch.int32, device=pooled_q.device)
+    call("fp_threshold_compact", _ptr(pooled_q), _ptr(pooled_k), nb, hq, hkv, d, float(softmax_scale),
+         float(alpha), int(n_sink), int(n_local), _ptr(idx), _ptr(counts), _stream(pooled_q))
+    return idx, counts
+
+
+def _attn(name, q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out, return_lse):
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if out is None:
+        out = torch.empty((L, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((hq, L), dtype=torch.float32, device=q.device) if return_lse else None
+    args = [_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+            L, hq, hkv, d, BLOCK, q.stride(0), q.stride(1), k.stride(0), k.stride(1),
+            v.stride(0), v.stride(1), out.stride(0), out.stride(1)]
+    if name == "fp_sparse_attn":
+        args += [_ptr(idx), _ptr(counts)]
+    args += [float(softmax_scale), _ptr(out), _ptr(lse), _stream(q)]
+    call(name, *args)
+    return (out, lse) if return_lse else out
+
+
+def sparse_attn(q, k, v, idx, counts, q_scale=None, k_scale=None, v_scale=None, softmax_scale=None,
+                out=None, return_lse=False):
+    """Causal GQA attention of Q [L, hq, 128] over the listed K/V blocks -> bf16 [L, hq, 128]."""
+    return _attn("fp_sparse_attn", q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out, return_lse)
+
+
+def dense_attn(q, k, v, q_scale=None, k_scale=None, v_scale=None, softmax_scale=None, out=None, return_lse=False):
+    """Dense causal GQA attention with the same kernel (implicit full lists)."""
+    return _attn("fp_dense_attn", q, k, v, None, None, q_scale, k_scale, v_scale, softmax_scale, out, return_lse)
+
+
+def prefill(q, k, v, alpha: float, n_sink: int = 1, n_local: int = 4, q_scale=None, k_scale=None, v_scale=None,
+            softmax_scale=None, return_lse=False):
+    """discover -> threshold_compact -> sparse_attn on one sequence."""
+    pq, pk = discover(q, k, q_scale, k_scale)
+    idx, counts = threshold_compact(pq, pk, alpha, n_sink, n_local, softmax_scale)
+    res = sparse_attn(q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, return_lse=return_lse)
+    return res, idx, counts
+
+
+# ------------------------------------------------------------ packed batches
+@dataclass
+class VarlenBatch:
+    """Host-side description of a packed batch; cu_seqlens lives on the device."""
+    lengths: Sequence[int]
+    device: torch.device
+
+    def __post_init__(self):
+        self.lengths = [int(x) for x in self.lengths]
+        cu = [0]
+        for n in self.lengths:
+            cu.append(cu[-1] + n)
+        self.cu_seqlens = torch.tensor(cu, dtype=torch.int32, device=self.device)
+        nbs = [_nb(n) for n in self.lengths]
+        self.seq_blocks = nbs
+        self.cu_blocks = [0]
+        self.cu_tri = [0]
+        for nb in nbs:
+            self.cu_blocks.append(self.cu_blocks[-1] + nb)
+            self.cu_tri.append(self.cu_tri[-1] + nb * (nb + 1) // 2)
+        self.n_seqs = len(self.lengths)
+        self.max_seqlen = max(self.lengths) if self.lengths else 0
+        self.total_tokens = cu[-1]
+        self.total_blocks = self.cu_blocks[-1]
+        self.total_tri = self.cu_tri[-1]
+
+
+def discover_paged(q, k, batch: VarlenBatch, page_table=None, q_scale=None, k_scale=None,
+                   pooled_q=None, pooled_k=None):
+    """Per-sequence pooling of packed Q [T, hq, 128] and K, either packed [T, hkv, 128]
+    (page_table None) or a page cache [P, 128, hkv, 128] -> ([hq, total_blocks, 128],
+    [hkv, total_blocks, 128]) fp64."""
+    T, hq, d = q.shape
+    if page_table is not None:
+        P, _, hkv, _ = k.shape
+        k_sp, k_st, k_sh = k.stride(0), k.stride(1), k.stride(2)
+        max_pages = page_table.shape[1]
+    else:
+        P, hkv = 0, k.shape[1]
+        k_sp, k_st, k_sh = 0, k.stride(0), k.stride(1)
+        max_pages = 0
+    if pooled_q is None:
+        pooled_q = torch.empty((hq, batch.total_blocks, d), dtype=torch.float64, device=q.device)
+    if pooled_k is None:
+        pooled_k = torch.empty((hkv, batch.total_blocks, d), dtype=torch.float64, device=q.device)
+    call("fp_discover_paged", _ptr(q), _ptr(k), _dtype_code(q), _ptr(q_scale), _ptr(k_scale),
+         _ptr(batch.cu_seqlens), batch.n_seqs, batch.max_seqlen, batch.total_tokens, batch.total_blocks,
+         _ptr(page_table), max_pages, P, hq, hkv, d, BLOCK, q.stride(0), q.stride(1), k_sp, k_st, k_sh,
+         _ptr(pooled_q), _ptr(pooled_k), _stream(q))
+    return pooled_q, pooled_k
+
+
+def threshold_compact_varlen(pooled_q, pooled_k, batch: VarlenBatch, alpha: float, n_sink: int, n_local: int,
+                             softmax_scale=None, idx=None, counts=None):
+    """Per-sequence lists -> (idx [hq * total_tri] int32, counts [hq, total_blocks] int32)."""
+    hq, _, d = pooled_q.shape
+    hkv = pooled_k.shape[0]
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if idx is None:
+        idx = torch.zeros(hq * batch.total_tri, dtype=torch.int32, device=pooled_q.device)
+    if counts is None:
+        counts = torch.empty((hq, batch.total_blocks), dtype=torch.int32, device=pooled_q.device)
+    call("fp_threshold_compact_varlen", _ptr(pooled_q), _ptr(pooled_k), _ptr(batch.cu_seqlens), batch.n_seqs,
+         batch.max_seqlen, batch.total_blocks, batch.total_tri, hq, hkv, d, float(softmax_scale), float(alpha),
+         int(n_sink), int(n_local), _ptr(idx), _ptr(counts), _stream(pooled_q))
+    return idx, counts
+
+
+def sparse_attn_paged(q, k, v, batch: VarlenBatch, idx=None, counts=None, page_table=None, q_scale=None,
+                      k_scale=None, v_scale=None, softmax_scale=None, out=None, return_lse=False):
+    """Per-sequence causal attention of packed Q over listed blocks (idx/counts None =
+    dense) with K/V packed or paged -> bf16 [T, hq, 128]."""
+    T, hq, d = q.shape
+    if page_table is not None:
+        P, _, hkv, _ = k.shape
+        ks = (k.stride(0), k.stride(1), k.stride(2))
+        vs = (v.stride(0), v.stride(1), v.stride(2))
+        max_pages = page_table.shape[1]
+    else:
+        P, hkv = 0, k.shape[1]
+        ks = (0, k.stride(0), k.stride(1))
+        vs = (0, v.stride(0), v.stride(1))
+        max_pages = 0
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    call("fp_sparse_attn_paged", _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(q_scale), _ptr(k_scale),
+         _ptr(v_scale), _ptr(batch.cu_seqlens), batch.n_seqs, batch.max_seqlen, batch.total_tokens,
+         batch.total_blocks, batch.total_tri, _ptr(page_table), max_pages, P, hq, hkv, d, BLOCK,
+         q.stride(0), q.stride(1), *ks, *vs, out.stride(0), out.stride(1), _ptr(idx), _ptr(counts),
+         float(softmax_scale), _ptr(out), _ptr(lse), _stream(q))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernels.
+// Not installed; the public contract is include/flashprefill.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fp {
+
+constexpr int kBlock = 128;   // tokens per block (= page size)
+constexpr int kHeadDim = 128; // head dimension
+
+// Sequence layout of a (possibly single-sequence) batch.
+struct SeqDesc {
+  const int32_t* cu_seqlens;  // device [n_seqs+1]; nullptr: one sequence of length L
+  int n_seqs;
+  int L;                      // the single sequence's length when cu_seqlens == nullptr
+  int max_nb;                 // ceil(max_seqlen / 128): grid extent over blocks
+  int64_t total_tokens;       // declared extents of the packed buffers
+  int64_t total_blocks;
+  int64_t total_tri;
+};
+
+// Paged KV addressing (table == nullptr: packed like Q).
+struct PageDesc {
+  const int32_t* table;       // device [n_seqs, max_pages]
+  int max_pages;
+  int num_pages;
+};
+
+struct PoolLaunch {
+  const void* x;              // [tokens, H, d] or pages [P, 128, H, d]
+  const float* scale;         // fp8 per-head scale or nullptr
+  int dtype;                  // 0 bf16, 1 fp8
+  int H;
+  int64_t st_page, st_tok, st_head;
+  bool paged;
+  double* out;                // [H, total_blocks, d]
+};
+
+struct SelectLaunch {
+  const double* pq;           // [hq, total_blocks, d]
+  const double* pk;           // [hkv, total_blocks, d]
+  int hq, hkv;
+  double scale;               // softmax scale applied to the pooled dot product
+  double log_alpha;           // ln(alpha), -inf for alpha == 0
+  int n_sink, n_local;
+  int32_t* idx;               // [hq, total_tri]
+  int32_t* counts;            // [hq, total_blocks]
+};
+
+struct AttnLaunch {
+  const void* q; const void* k; const void* v;
+  const float* q_scale; const float* k_scale; const float* v_scale;
+  int dtype;
+  int hq, hkv;
+  int64_t q_st, q_sh;
+  int64_t k_sp, k_st, k_sh;
+  int64_t v_sp, v_st, v_sh;
+  int64_t o_st, o_sh;
+  const int32_t* idx;         // nullptr: dense (implicit list 0..i)
+  const int32_t* counts;
+  float softmax_scale;
+  void* out;
+  float* lse;                 // [hq, total_tokens] or nullptr
+};
+
+hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);
+hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st);
+hipError_t launch_attn(const AttnLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);
+
+}  // namespace fp

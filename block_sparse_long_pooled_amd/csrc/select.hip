@@ -1,0 +1,163 @@
+// Pooled block scores, dynamic threshold and index compaction (FlashPrefill
+// Method 1 pooled score map, Method 2 "Dynamic Threshold Pruning": keep a
+// block when its score reaches alpha times the row maximum, always keep the
+// attention sinks and the local window; Method 3 "Index Compaction": write
+// the kept block ids of every row into a contiguous ascending list).
+//
+// One workgroup owns a tile of 64 query blocks of one (sequence, query head)
+// and sweeps the causal key-block tiles 0..(its own) twice: pass 1 computes
+// the fp64 scores and the row maxima, pass 2 recomputes them, tests
+// s - max >= ln(alpha) (or sink / local), and compacts.  Scores are fp64 dot
+// products of the fp64 pooled means, tiled 64x64 with a 16-wide d-chunk in
+// LDS; each thread owns a 4x4 sub-tile.  Compaction: the 16 lanes that share
+// a row hold 4 consecutive columns each, so a 16-lane exclusive prefix sum of
+// the per-lane keep counts gives every kept id its slot, ascending by
+// construction.
+#include "fp_device.h"
+
+namespace fp {
+namespace {
+
+constexpr int kTile = 64;
+constexpr int kDK = 16;
+constexpr int kThreads = 256;
+
+struct SelK {
+  SelectLaunch a;
+  SeqDesc sd;
+};
+
+// acc[4][4] = Qtile(rows tr*4..) x Ktile(cols tc*4..)^T for one (row tile, col tile).
+__device__ inline void tile_scores(const double* __restrict__ Qb, const double* __restrict__ Kb,
+                                   int row0, int col0, int nb, double (*Qs)[kTile], double (*Ks)[kTile],
+                                   double acc[4][4]) {
+  const int tid = threadIdx.x;
+  const int tr = tid >> 4, tc = tid & 15;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  for (int dk0 = 0; dk0 < kHeadDim; dk0 += kDK) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + u * kThreads;  // 0..1023 = 64 rows x 16 d
+      const int rr = e >> 4, dd = e & 15;
+      const int qi = row0 + rr, kj = col0 + rr;
+      Qs[dd][rr] = qi < nb ? Qb[(int64_t)qi * kHeadDim + dk0 + dd] : 0.0;
+      Ks[dd][rr] = kj < nb ? Kb[(int64_t)kj * kHeadDim + dk0 + dd] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int dd = 0; dd < kDK; ++dd) {
+      double qv[4], kv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qv[x] = Qs[dd][tr * 4 + x];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) kv[y] = Ks[dd][tc * 4 + y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(qv[x], kv[y], acc[x][y]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
+  const SelectLaunch& a = p.a;
+  const int it = blockIdx.x;
+  const int s = blockIdx.y;
+  const int h = blockIdx.z;
+  const SeqPos sp = seq_pos(p.sd, s);
+  const int nb = (sp.len + kBlock - 1) / kBlock;
+  const int row0 = it * kTile;
+  if (row0 >= nb) return;
+  const int g = h / (a.hq / a.hkv);
+  const double* Qb = a.pq + ((int64_t)h * p.sd.total_blocks + sp.blk0) * kHeadDim;
+  const double* Kb = a.pk + ((int64_t)g * p.sd.total_blocks + sp.blk0) * kHeadDim;
+
+  __shared__ double Qs[kDK][kTile];
+  __shared__ double Ks[kDK][kTile];
+
+  const int tid = threadIdx.x;
+  const int tr = tid >> 4, tc = tid & 15;
+  const double NEG_INF = -__builtin_huge_val();
+
+  // pass 1: row maxima over the causal blocks j <= i
+  double rmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+  double acc[4][4];
+  for (int jt = 0; jt <= it; ++jt) {
+    tile_scores(Qb, Kb, row0, jt * kTile, nb, Qs, Ks, acc);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = row0 + tr * 4 + x;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int j = jt * kTile + tc * 4 + y;
+        if (j <= i && i < nb) rmax[x] = fmax(rmax[x], acc[x][y] * a.scale);
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) rmax[x] = fmax(rmax[x], __shfl_xor(rmax[x], off, 16));
+
+  // pass 2: threshold + compaction
+  int cnt[4] = {0, 0, 0, 0};
+  int32_t* idx_h = a.idx + (int64_t)h * p.sd.total_tri + sp.tri0;
+  const int64_t tri_cap = p.sd.total_tri - sp.tri0;
+  for (int jt = 0; jt <= it; ++jt) {
+    tile_scores(Qb, Kb, row0, jt * kTile, nb, Qs, Ks, acc);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = row0 + tr * 4 + x;
+      unsigned bits = 0;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int j = jt * kTile + tc * 4 + y;
+        const double sc = acc[x][y] * a.scale;
+        const bool keep = (j <= i) && (i < nb) &&
+                          ((sc - rmax[x] >= a.log_alpha) || (j < a.n_sink) || (j > i - a.n_local));
+        bits |= (keep ? 1u : 0u) << y;
+      }
+      const int pc = __popc(bits);
+      int incl = pc;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const int v = __shfl_up(incl, off, 16);
+        if (tc >= off) incl += v;
+      }
+      const int total = __shfl(incl, 15, 16);
+      int pos = cnt[x] + incl - pc;
+      const int64_t rbase = (int64_t)i * (i + 1) / 2;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        if (bits & (1u << y)) {
+          if (rbase + pos < tri_cap) idx_h[rbase + pos] = jt * kTile + tc * 4 + y;
+          ++pos;
+        }
+      }
+      cnt[x] += total;
+    }
+  }
+  if (tc == 0) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = row0 + tr * 4 + x;
+      if (i < nb && sp.blk0 + i < p.sd.total_blocks)
+        a.counts[(int64_t)h * p.sd.total_blocks + sp.blk0 + i] = cnt[x];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st) {
+  SelK p{a, sd};
+  dim3 grid((sd.max_nb + kTile - 1) / kTile, sd.n_seqs, a.hq);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace fp

@@ -1,0 +1,227 @@
+/*
+ * flashprefill.h -- C ABI of the MI355X (gfx950) FlashPrefill block-sparse
+ * prefill-attention library (libflashprefill.so).
+ *
+ * The path has three calls, each one stage of the method:
+ *   fp_discover            mean-pool Q and K per 128-token block
+ *   fp_threshold_compact   pooled block scores, max-relative threshold with
+ *                          sink / local-window blocks, ascending list compaction
+ *   fp_sparse_attn         causal GQA flash attention over the listed blocks
+ * plus fp_dense_attn (implicit full causal list, the same-GPU dense baseline)
+ * and paged-KV / continuous-batching variants of each.
+ *
+ * Sources: "FlashPrefill: Near-Zero-Cost Sparsity Discovery for Ultra-Fast
+ * Long-Context Prefilling" (zhichai.net), sections Method 1 (instantaneous
+ * pattern discovery), 2 (dynamic threshold pruning), 3 (index compaction ->
+ * physical jumps); "FlashPrefill V2: Block-Sparse Prefill Attention for
+ * Long-Context LLM Serving" (shd-paper.top, English abstract): FP8 inference,
+ * paged KV cache and continuous batching.
+ *
+ * Conventions shared by every call
+ *   - Every tensor argument is a DEVICE pointer owned by the caller.  Nothing
+ *     is allocated, freed or synchronised inside the library; each call only
+ *     enqueues kernels on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream) and returns.  There is no global mutable state apart
+ *     from a thread-local error message, so calls from several host threads
+ *     are safe.
+ *   - Head dimension d and block size B must both be 128.  hq % hkv == 0;
+ *     query head h reads KV head h / (hq / hkv).
+ *   - Strides are in ELEMENTS; the innermost (head-dim) stride is 1.  Data
+ *     pointers must be 16-byte aligned and the token/head/page strides must
+ *     keep every 128-element head row 16-byte aligned.
+ *   - dtype: FP_BF16 (bfloat16 inputs) or FP_FP8_E4M3 (OCP e4m3fn codes,
+ *     max 448, with one fp32 scale per head: value = code * scale).  Scales
+ *     are device arrays and must be finite and > 0.  Outputs are bf16.
+ *   - Return value: FP_OK, or an error code.  All argument checks happen on
+ *     the host before anything is enqueued; an error leaves every output
+ *     untouched.  FP_EHIP reports a failed kernel launch.  No call aborts or
+ *     throws.  fp_last_error() returns a description of the last failure on
+ *     the calling thread.
+ *   - nb = ceil(L / 128) blocks per sequence.  Lists are stored triangular-
+ *     packed: the list of (query head h, query block i) of a single sequence
+ *     starts at idx[h * nb*(nb+1)/2 + i*(i+1)/2] and holds counts[h*nb + i]
+ *     ascending block ids; the last one is always i.
+ *
+ * Numerics
+ *   - Pooled means are fp64.  Sums of up to 128 bf16 values (or e4m3 codes)
+ *     are exact in fp64, so the means are the exact means rounded once.
+ *   - Block scores are fp64; the threshold test is s_ij - max_j s_ij >= ln(alpha)
+ *     (alpha = 0 keeps every causal block).
+ *   - Attention: MFMA products with fp32 accumulation, fp32 online softmax,
+ *     probabilities rounded to bf16 (bf16 path) or e4m3 (fp8 path) for the
+ *     P*V product, bf16 output, optional fp32 log-sum-exp (natural log).
+ */
+#ifndef FLASHPREFILL_H
+#define FLASHPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp_status {
+  FP_OK = 0,
+  FP_EINVAL = 1,        /* invalid argument (null pointer, bad size, stride, alignment, alpha) */
+  FP_EUNSUPPORTED = 2,  /* valid but not supported here (d != 128, B != 128, unknown dtype)  */
+  FP_EHIP = 3           /* a HIP runtime call or kernel launch failed                        */
+};
+
+enum fp_dtype {
+  FP_BF16 = 0,
+  FP_FP8_E4M3 = 1       /* OCP e4m3fn codes + fp32 per-head scales */
+};
+
+/* Human-readable name of a status code (static string). */
+const char* fp_status_string(int status);
+/* Description of the last error returned on this host thread ("" if none). */
+const char* fp_last_error(void);
+/* Library ABI version (increments on any signature change). */
+int fp_abi_version(void);
+
+/* Host helpers: number of blocks ceil(L / block), and the idx capacity in
+ * int32 elements for one sequence: hq * nb * (nb + 1) / 2. */
+int64_t fp_num_blocks(int64_t L, int block);
+int64_t fp_idx_capacity(int hq, int64_t nb);
+
+/* ---------------------------------------------------------------------------
+ * fp_discover -- block mean pooling of Q and K (Method 1: each block of B
+ * tokens is represented by the mean of its vectors; "mean-proxy").
+ *
+ *   q          [L, hq, d] at q + t*q_stride_tok + h*q_stride_head
+ *   k          [L, hkv, d] likewise
+ *   q_scale    fp8 only: [hq] fp32 (ignored for bf16, may be NULL)
+ *   k_scale    fp8 only: [hkv] fp32
+ *   pooled_q   out [hq, nb, d] fp64, contiguous: mean of the block's tokens
+ *   pooled_k   out [hkv, nb, d] fp64, contiguous
+ * A partial last block is averaged over its valid tokens.
+ * ------------------------------------------------------------------------- */
+int fp_discover(const void* q, const void* k, int dtype,
+                const float* q_scale, const float* k_scale,
+                int L, int hq, int hkv, int d, int block,
+                int64_t q_stride_tok, int64_t q_stride_head,
+                int64_t k_stride_tok, int64_t k_stride_head,
+                double* pooled_q, double* pooled_k, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * fp_threshold_compact -- pooled block scores, dynamic threshold and index
+ * compaction (Methods 1-3).
+ *
+ *   s_ij  = softmax_scale * pooled_q[h, i] . pooled_k[h / (hq/hkv), j],  j <= i
+ *   keep  = (s_ij - max_{j'<=i} s_ij' >= ln(alpha))      threshold alpha x row max
+ *           or j < n_sink                                  attention sinks
+ *           or j > i - n_local                             local window (diagonal incl.)
+ *   idx    out: ascending kept j per (h, i), triangular-packed (see above);
+ *          capacity fp_idx_capacity(hq, nb) int32
+ *   counts out: [hq, nb] int32 list lengths (>= 1)
+ *
+ * alpha must be finite and >= 0 (alpha = 0 keeps every causal block, alpha > 1
+ * keeps only the forced blocks); n_sink >= 0; n_local >= 1.  softmax_scale
+ * must be finite and > 0 (normally 1/sqrt(d)).
+ * ------------------------------------------------------------------------- */
+int fp_threshold_compact(const double* pooled_q, const double* pooled_k,
+                         int nb, int hq, int hkv, int d,
+                         double softmax_scale, double alpha, int n_sink, int n_local,
+                         int32_t* idx, int32_t* counts, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * fp_sparse_attn -- causal GQA block-sparse flash attention (Method 3: the
+ * inner loop visits only the listed key blocks, "physical jumps").
+ *
+ *   O[t, h] = sum_{c in C(t)} softmax_c(softmax_scale * q_t . k_c) v_c,
+ *   C(t)    = { c <= t : c / B in list(h, t / B) }.
+ *
+ *   q, o       [L, hq, d];  k, v [L, hkv, d]  (strided as in fp_discover)
+ *   idx/counts the lists from fp_threshold_compact (each list ascending, each
+ *              id in [0, i], ending with i)
+ *   v_scale    fp8 only: [hkv] fp32
+ *   out        bf16 [L, hq, d] at out + t*o_stride_tok + h*o_stride_head
+ *   lse        optional (NULL = skip): fp32 [hq, L], natural-log log-sum-exp of
+ *              the scaled logits of each query row
+ * ------------------------------------------------------------------------- */
+int fp_sparse_attn(const void* q, const void* k, const void* v, int dtype,
+                   const float* q_scale, const float* k_scale, const float* v_scale,
+                   int L, int hq, int hkv, int d, int block,
+                   int64_t q_stride_tok, int64_t q_stride_head,
+                   int64_t k_stride_tok, int64_t k_stride_head,
+                   int64_t v_stride_tok, int64_t v_stride_head,
+                   int64_t o_stride_tok, int64_t o_stride_head,
+                   const int32_t* idx, const int32_t* counts, float softmax_scale,
+                   void* out, float* lse, void* stream);
+
+/* fp_dense_attn -- the same kernel with the implicit full causal list
+ * {0..i} for every query block: plain causal GQA attention.  Arguments as in
+ * fp_sparse_attn without idx/counts. */
+int fp_dense_attn(const void* q, const void* k, const void* v, int dtype,
+                  const float* q_scale, const float* k_scale, const float* v_scale,
+                  int L, int hq, int hkv, int d, int block,
+                  int64_t q_stride_tok, int64_t q_stride_head,
+                  int64_t k_stride_tok, int64_t k_stride_head,
+                  int64_t v_stride_tok, int64_t v_stride_head,
+                  int64_t o_stride_tok, int64_t o_stride_head,
+                  float softmax_scale, void* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Continuous batching and paged KV (V2 abstract: native paged KV cache and
+ * continuous batching).  A batch of n_seqs sequences is packed token-major:
+ *
+ *   cu_seqlens  device int32 [n_seqs + 1], cu_seqlens[0] = 0, non-decreasing,
+ *               cu_seqlens[n_seqs] = total_tokens; sequence s owns tokens
+ *               cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed Q (and of the
+ *               packed K/V when page_table is NULL).  Queries and keys of a
+ *               sequence both start at its token 0 (prefill).
+ *   max_seqlen  host int >= every sequence length (sizes the launch grid).
+ *   Blocks: nb_s = ceil(len_s / B); block i of sequence s has packed block id
+ *               cu_blocks[s] + i with cu_blocks[s] = sum_{r<s} nb_r, and
+ *               total_blocks = sum_s nb_s.
+ *   Lists:  the list of (h, s, i) starts at
+ *               idx[h * total_tri + cu_tri[s] + i*(i+1)/2]
+ *           with cu_tri[s] = sum_{r<s} nb_r*(nb_r+1)/2, total_tri = sum_s
+ *           nb_s*(nb_s+1)/2; counts are [hq, total_blocks].
+ *   Paging: when page_table is non-NULL, K and V are caches of 128-token pages
+ *           [num_pages, 128, hkv, d] addressed by (page, row, head) strides,
+ *           and logical block j of sequence s lives in page
+ *           page_table[s * max_pages + j].  A page id outside [0, num_pages)
+ *           is never dereferenced; the outputs that depend on it are NaN.
+ *           When page_table is NULL, K and V are packed [total_tokens, hkv, d]
+ *           like Q (the stride_page arguments are ignored).
+ * The host cannot see device metadata: total_tokens / total_blocks / total_tri
+ * are the caller's declared extents and kernels never access beyond them.
+ * ------------------------------------------------------------------------- */
+int fp_discover_paged(const void* q, const void* k, int dtype,
+                      const float* q_scale, const float* k_scale,
+                      const int32_t* cu_seqlens, int n_seqs, int max_seqlen,
+                      int64_t total_tokens, int64_t total_blocks,
+                      const int32_t* page_table, int max_pages, int num_pages,
+                      int hq, int hkv, int d, int block,
+                      int64_t q_stride_tok, int64_t q_stride_head,
+                      int64_t k_stride_page, int64_t k_stride_tok, int64_t k_stride_head,
+                      double* pooled_q, double* pooled_k, void* stream);
+
+int fp_threshold_compact_varlen(const double* pooled_q, const double* pooled_k,
+                                const int32_t* cu_seqlens, int n_seqs, int max_seqlen,
+                                int64_t total_blocks, int64_t total_tri,
+                                int hq, int hkv, int d,
+                                double softmax_scale, double alpha, int n_sink, int n_local,
+                                int32_t* idx, int32_t* counts, void* stream);
+
+/* idx == NULL and counts == NULL selects the implicit full causal list (dense). */
+int fp_sparse_attn_paged(const void* q, const void* k, const void* v, int dtype,
+                         const float* q_scale, const float* k_scale, const float* v_scale,
+                         const int32_t* cu_seqlens, int n_seqs, int max_seqlen,
+                         int64_t total_tokens, int64_t total_blocks, int64_t total_tri,
+                         const int32_t* page_table, int max_pages, int num_pages,
+                         int hq, int hkv, int d, int block,
+                         int64_t q_stride_tok, int64_t q_stride_head,
+                         int64_t k_stride_page, int64_t k_stride_tok, int64_t k_stride_head,
+                         int64_t v_stride_page, int64_t v_stride_tok, int64_t v_stride_head,
+                         int64_t o_stride_tok, int64_t o_stride_head,
+                         const int32_t* idx, const int32_t* counts, float softmax_scale,
+                         void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHPREFILL_H */

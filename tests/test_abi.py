@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/flashprefill.h declares, and rejects invalid arguments on the host before
+anything is enqueued (these calls never reach a kernel launch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_long_pooled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashprefill.h")
+
+# A fake but 16-byte aligned "device" address: validation never dereferences pointers.
+P = 0x10000
+EINVAL, EUNSUP = _lib.FP_EINVAL, _lib.FP_EUNSUPPORTED
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(fp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for n in ["fp_discover", "fp_threshold_compact", "fp_sparse_attn", "fp_dense_attn",
+              "fp_discover_paged", "fp_threshold_compact_varlen", "fp_sparse_attn_paged"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_status_strings_and_helpers():
+    lib = _lib.load()
+    assert lib.fp_status_string(0) == b"FP_OK"
+    assert lib.fp_status_string(1) == b"FP_EINVAL"
+    assert lib.fp_abi_version() >= 1
+    assert lib.fp_num_blocks(131072, 128) == 1024
+    assert lib.fp_num_blocks(1000, 128) == 8
+    assert lib.fp_idx_capacity(32, 1024) == 32 * 1024 * 1025 // 2
+
+
+def discover(**kw):
+    a = dict(q=P, k=P, dtype=0, qs=None, ks=None, L=4096, hq=4, hkv=2, d=128, block=128,
+             qst=512, qsh=128, kst=256, ksh=128, pq=P, pk=P, stream=None)
+    a.update(kw)
+    return _lib.status_of("fp_discover", a["q"], a["k"], a["dtype"], a["qs"], a["ks"], a["L"], a["hq"], a["hkv"],
+                          a["d"], a["block"], a["qst"], a["qsh"], a["kst"], a["ksh"], a["pq"], a["pk"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), EUNSUP), (dict(block=64), EUNSUP), (dict(dtype=7), EUNSUP),
+    (dict(hq=3, hkv=2), EINVAL), (dict(hkv=0), EINVAL), (dict(q=None), EINVAL), (dict(pk=None), EINVAL),
+    (dict(q=P + 2), EINVAL), (dict(qst=511), EINVAL), (dict(ksh=-128), EINVAL), (dict(L=-1), EINVAL),
+    (dict(dtype=1), EINVAL),  # fp8 without scales
+    (dict(dtype=1, qs=P, ks=P, qst=520), EINVAL),  # fp8 rows need 16-element alignment
+])
+def test_discover_rejects(kw, code):
+    assert discover(**kw) == code
+    assert _lib.load().fp_last_error()
+
+
+def select(**kw):
+    a = dict(pq=P, pk=P, nb=32, hq=4, hkv=2, d=128, scale=1 / math.sqrt(128), alpha=0.1, ns=1, nl=2,
+             idx=P, cnt=P, stream=None)
+    a.update(kw)
+    return _lib.status_of("fp_threshold_compact", a["pq"], a["pk"], a["nb"], a["hq"], a["hkv"], a["d"],
+                          a["scale"], a["alpha"], a["ns"], a["nl"], a["idx"], a["cnt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha=-0.1), EINVAL), (dict(alpha=float("nan")), EINVAL), (dict(alpha=float("inf")), EINVAL),
+    (dict(nl=0), EINVAL), (dict(ns=-1), EINVAL), (dict(scale=0.0), EINVAL), (dict(idx=None), EINVAL),
+    (dict(cnt=None), EINVAL), (dict(d=96), EUNSUP), (dict(hq=5, hkv=2), EINVAL), (dict(nb=-3), EINVAL),
+])
+def test_threshold_rejects(kw, code):
+    assert select(**kw) == code
+
+
+def attn(name="fp_sparse_attn", **kw):
+    a = dict(q=P, k=P, v=P, dtype=0, qs=None, ks=None, vs=None, L=1024, hq=4, hkv=2, d=128, block=128,
+             st=[512, 128, 256, 128, 256, 128, 512, 128], idx=P, cnt=P, scale=0.088, out=P, lse=None, stream=None)
+    a.update(kw)
+    args = [a["q"], a["k"], a["v"], a["dtype"], a["qs"], a["ks"], a["vs"], a["L"], a["hq"], a["hkv"], a["d"],
+            a["block"], *a["st"]]
+    if name == "fp_sparse_attn":
+        args += [a["idx"], a["cnt"]]
+    args += [a["scale"], a["out"], a["lse"], a["stream"]]
+    return _lib.status_of(name, *args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), EINVAL), (dict(out=None), EINVAL), (dict(v=P + 8), EINVAL),
+    (dict(scale=-1.0), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(dtype=1), EINVAL),
+    (dict(st=[512, 128, 256, 128, 256, 128, 512, 4]), EINVAL), (dict(lse=P + 2), EINVAL),
+    (dict(d=256), EUNSUP), (dict(hq=4, hkv=3), EINVAL),
+])
+def test_sparse_attn_rejects(kw, code):
+    assert attn(**kw) == code
+
+
+def test_dense_attn_rejects():
+    assert attn("fp_dense_attn", out=None) == EINVAL
+    assert attn("fp_dense_attn", block=256) == EUNSUP
+
+
+def test_paged_rejects():
+    lib = _lib.load()
+    # page table given but max_pages smaller than ceil(max_seqlen / 128)
+    rc = lib.fp_sparse_attn_paged(P, P, P, 0, None, None, None, P, 2, 1000, 1500, 12, 78, P, 3, 20, 4, 2, 128, 128,
+                                  512, 128, 32768, 256, 128, 32768, 256, 128, 512, 128, P, P, 0.088, P, None, None)
+    assert rc == EINVAL and b"max_pages" in lib.fp_last_error()
+    # no cu_seqlens
+    rc = lib.fp_discover_paged(P, P, 0, None, None, None, 2, 1000, 1500, 12, None, 0, 0, 4, 2, 128, 128,
+                               512, 128, 0, 256, 128, P, P, None)
+    assert rc == EINVAL
+    # n_seqs out of range
+    rc = lib.fp_threshold_compact_varlen(P, P, P, 0, 1000, 12, 78, 4, 2, 128, 0.088, 0.1, 1, 1, P, P, None)
+    assert rc == EINVAL
+
+
+def test_empty_inputs_are_a_no_op():
+    """L = 0 validates and returns FP_OK without launching anything."""
+    assert discover(L=0) == _lib.FP_OK
+    assert select(nb=0) == _lib.FP_OK
+    assert attn(L=0) == _lib.FP_OK
