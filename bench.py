@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashPrefill block-sparse prefill hot path on one MI355X.
+
+One step = discover (pool Q/K) -> threshold_compact (scores, alpha x row-max
+threshold, sink/local blocks, lists) -> sparse_attn (causal GQA attention over
+the lists), on the Qwen3-30B-A3B-shaped 128K workload: 32 query / 4 KV heads,
+d = 128, L = 131072, B = 128, bf16, alpha = 0.1, 1 sink block, 4 local blocks,
+seeded block-structured synthetic inputs (synth.make_config(2)) resident in
+HBM before timing starts.
+
+Prints ONE JSON line.  `value` is dense-equivalent TFLOP/s of the whole step
+(2 * hq * d * L^2 causal flops / step time).  `roofline` is for the dominant
+kernel (the sparse attention): computed MFMA flops per launch
+(sum(counts) * 4 * B^2 * d) over its mean launch time, measured with HIP
+events on the stream the kernels run on.  `cpu_baseline` times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+BLOCK = 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2 = 128K bf16)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the same-GPU dense comparison")
+    ap.add_argument("--no-extra", action="store_true", help="skip the fp8 256K side measurement")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of sampled oracle attention")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_hot_path(wl, steps, warmup, alpha):
+    """Run the hot path `warmup` + `steps` times; per-stage HIP-event timing."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    import synth
+
+    dev = torch.device("cuda", 0)
+    q, k, v, qs, ks, vs = synth.device_tensors(wl, dev)
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    nb = -(-L // BLOCK)
+    pq = torch.empty((hq, nb, d), dtype=torch.float64, device=dev)
+    pk = torch.empty((hkv, nb, d), dtype=torch.float64, device=dev)
+    idx = torch.zeros(fp.idx_capacity(hq, nb), dtype=torch.int32, device=dev)
+    counts = torch.empty((hq, nb), dtype=torch.int32, device=dev)
+    out = torch.empty((L, hq, d), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fp.discover(q, k, qs, ks, pooled_q=pq, pooled_k=pk)
+        if ev is not None:
+            ev[1].record()
+        fp.threshold_compact(pq, pk, alpha, wl.n_sink, wl.n_local, idx=idx, counts=counts)
+        if ev is not None:
+            ev[2].record()
+        fp.sparse_attn(q, k, v, idx, counts, qs, ks, vs, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(steps):
+        step(evs[s])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1) / steps
+    stage = np.array([[e[x].elapsed_time(e[x + 1]) for x in range(3)] for e in evs])
+    res = dict(ms_per_step=total_ms, wall_s=wall, disc_ms=float(stage[:, 0].mean()),
+               thr_ms=float(stage[:, 1].mean()), attn_ms=float(stage[:, 2].mean()),
+               attn_ms_min=float(stage[:, 2].min()), sum_counts=int(counts.sum().item()), nb=nb)
+    res["counts"] = counts
+    res["tensors"] = (q, k, v, qs, ks, vs, out)
+    return res
+
+
+def time_dense(tensors, reps=2):
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    q, k, v, qs, ks, vs, out = tensors
+    fp.dense_attn(q, k, v, qs, ks, vs, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fp.dense_attn(q, k, v, qs, ks, vs, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(wl, alpha, dense_eq_flops, budget_s):
+    """fp64 oracle on the host: pooling, scores, threshold and lists on the whole
+    input; sparse attention on seeded sampled (head, query block) rows within a time
+    budget, extrapolated to all rows by the number of listed blocks."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    q = O.decode_bf16(wl.q) if wl.dtype == "bf16" else O.dequantize(wl.q, wl.q_scale)
+    k = O.decode_bf16(wl.k) if wl.dtype == "bf16" else O.dequantize(wl.k, wl.k_scale)
+    v = O.decode_bf16(wl.v) if wl.dtype == "bf16" else O.dequantize(wl.v, wl.v_scale)
+    t = time.perf_counter()
+    sel = O.select_blocks(q, k, BLOCK, alpha, wl.n_sink, wl.n_local)
+    t_sel = time.perf_counter() - t
+    counts = sel["counts"]
+    hq, nb = counts.shape
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(hq * nb)
+    t_att = 0.0
+    done_blocks = 0
+    rows = 0
+    for r in order:
+        h, i = divmod(int(r), nb)
+        t = time.perf_counter()
+        O.attend_block(q, k, v, sel["lists"][h][i], h, i, BLOCK)
+        t_att += time.perf_counter() - t
+        done_blocks += int(counts[h, i])
+        rows += 1
+        if t_att >= budget_s:
+            break
+    total_blocks = int(counts.sum())
+    t_att_all = t_att * total_blocks / max(done_blocks, 1)
+    t_all = t_sel + t_att_all
+    return {
+        "value": dense_eq_flops / t_all / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(cores),
+        "kind": "oracle",
+        "ms_per_step": t_all * 1e3,
+        "sample": (f"fp64 oracle: pooling+scores+threshold+lists on all {hq}x{nb} rows ({t_sel:.1f} s); "
+                   f"sparse attention on {rows} seeded random (head, query-block) rows = "
+                   f"{100.0 * done_blocks / total_blocks:.2f}% of listed blocks ({t_att:.1f} s), "
+                   f"extrapolated by listed-block count"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch  # noqa: F401
+
+    import synth
+
+    t = time.perf_counter()
+    wl = synth.make_config(args.config)
+    log(f"generated {wl.name} in {time.perf_counter() - t:.1f}s")
+    alpha = wl.alphas[len(wl.alphas) // 2] if len(wl.alphas) > 1 else wl.alphas[0]
+    assert wl.n_seqs == 1, "bench times the single-sequence configurations"
+    L, hq, hkv, d = wl.L, wl.hq, wl.hkv, wl.d
+    dense_eq = 2.0 * hq * d * L * L
+    r = time_hot_path(wl, args.steps, args.warmup, alpha)
+    log(f"stages ms: discover {r['disc_ms']:.3f} threshold {r['thr_ms']:.3f} attn {r['attn_ms']:.3f}")
+    nb = r["nb"]
+    density = r["sum_counts"] / (hq * nb * (nb + 1) / 2)
+    computed_flops = r["sum_counts"] * 4.0 * BLOCK * BLOCK * d
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP8_TFLOPS
+    attn_tflops = computed_flops / (r["attn_ms"] * 1e-3) / 1e12
+    esize = 2 if wl.dtype == "bf16" else 1
+    disc_bytes = L * (hq + hkv) * d * esize + (hq + hkv) * nb * d * 8
+    disc_gbs = disc_bytes / (r["disc_ms"] * 1e-3) / 1e9
+
+    extra = {
+        "stage_ms": {"discover": r["disc_ms"], "threshold_compact": r["thr_ms"], "sparse_attn": r["attn_ms"]},
+        "density": density,
+        "attn_ms": r["attn_ms"],
+        "attn_dense_equiv_tflops": dense_eq / (r["attn_ms"] * 1e-3) / 1e12,
+        "attn_computed_tflops": attn_tflops,
+        "mfma_frac": attn_tflops / peak,
+        "discover_gbs": disc_gbs,
+        "discover_hbm_frac": disc_gbs / PEAK_HBM_GBS,
+        "selection_overhead_frac": (r["disc_ms"] + r["thr_ms"]) / r["ms_per_step"],
+    }
+    if not args.no_dense:
+        dms = time_dense(r["tensors"])
+        extra["dense_attn_ms"] = dms
+        extra["dense_attn_tflops"] = dense_eq / (dms * 1e-3) / 1e12
+        extra["dense_attn_mfma_frac"] = extra["dense_attn_tflops"] / peak
+        extra["speedup_vs_dense_step"] = dms / r["ms_per_step"]
+        log(f"dense attention {dms:.2f} ms")
+    del r["tensors"]
+
+    if not args.no_extra and args.config == 2:
+        import torch
+        torch.cuda.empty_cache()
+        wl8 = synth.make_config(3)
+        r8 = time_hot_path(wl8, max(2, args.steps // 2), 1, wl8.alphas[0])
+        nb8 = r8["nb"]
+        L8 = wl8.L
+        c8 = r8["sum_counts"] * 4.0 * BLOCK * BLOCK * d
+        extra["fp8_256k"] = {
+            "workload": wl8.name, "ms_per_step": r8["ms_per_step"],
+            "dense_equiv_tflops": 2.0 * wl8.hq * d * L8 * L8 / (r8["ms_per_step"] * 1e-3) / 1e12,
+            "stage_ms": {"discover": r8["disc_ms"], "threshold_compact": r8["thr_ms"], "sparse_attn": r8["attn_ms"]},
+            "density": r8["sum_counts"] / (wl8.hq * nb8 * (nb8 + 1) / 2),
+            "attn_computed_tflops": c8 / (r8["attn_ms"] * 1e-3) / 1e12,
+            "mfma_frac_fp8": c8 / (r8["attn_ms"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+        }
+        del r8["tensors"], wl8
+        log(f"fp8 256K step {extra['fp8_256k']['ms_per_step']:.2f} ms")
+
+    line = {
+        "metric": "prefill attn ms & dense-equiv TFLOP/s at 128K GQA bf16/fp8; MFMA util",
+        "value": dense_eq / (r["ms_per_step"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent, whole hot path)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "hq": hq, "hkv": hkv, "head_dim": d, "seq_len": L, "block": BLOCK,
+                   "alpha": alpha, "n_sink": wl.n_sink, "n_local": wl.n_local, "batch": 1,
+                   "step": "discover + threshold_compact + sparse_attn"},
+        "roofline": {
+            "kernel": "attn_kernel (sparse, bf16)" if wl.dtype == "bf16" else "attn_kernel (sparse, fp8)",
+            "bound": "mfma", "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
+            "frac": attn_tflops / peak, "traffic": None,
+        },
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(wl, alpha, dense_eq, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

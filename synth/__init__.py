@@ -342,3 +342,30 @@ def make_config(k: int, threads: int = 8) -> Workload:
         return make_workload(name, 32, 4, config_lengths(4), seed=seed, paged=True,
                              alphas=(0.1,), n_sink=1, n_local=4, threads=threads)
     raise ValueError(f"unknown config {k}")
+
+
+def device_tensors(wl: Workload, device="cuda"):
+    """(q, k, v, q_scale, k_scale, v_scale) as torch tensors on `device`: bf16 bit
+    patterns as torch.bfloat16, fp8 as uint8 e4m3fn codes plus fp32 scales."""
+    import torch
+
+    if wl.dtype == "bf16":
+        def conv(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        sc = (None, None, None)
+    else:
+        def conv(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        sc = tuple(torch.from_numpy(s).to(device) for s in (wl.q_scale, wl.k_scale, wl.v_scale))
+    return (conv(wl.q), conv(wl.k), conv(wl.v)) + sc
+
+
+def device_pages(wl: Workload, device="cuda"):
+    """(k_cache, v_cache, page_table) of a paged bf16 workload as torch tensors."""
+    import torch
+
+    assert wl.paged and wl.dtype == "bf16"
+
+    def conv(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return conv(wl.k_cache), conv(wl.v_cache), torch.from_numpy(wl.page_table).to(device)

@@ -7,6 +7,7 @@ import numpy as np
 import torch
 
 import oracle as O
+import synth
 
 BAND_REL = 1e-6
 TOL_BF16 = 2e-2
@@ -18,25 +19,11 @@ def have_gpu() -> bool:
 
 
 def to_device(wl, device="cuda"):
-    """(q, k, v, q_scale, k_scale, v_scale) torch tensors on the device; bf16 as
-    torch.bfloat16, fp8 as uint8 e4m3fn codes + fp32 scales."""
-    if wl.dtype == "bf16":
-        def conv(a):
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
-        sc = (None, None, None)
-    else:
-        def conv(a):
-            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
-        sc = tuple(torch.from_numpy(s).to(device) for s in (wl.q_scale, wl.k_scale, wl.v_scale))
-    return (conv(wl.q), conv(wl.k), conv(wl.v)) + sc
+    return synth.device_tensors(wl, device)
 
 
 def to_device_paged(wl, device="cuda"):
-    assert wl.paged and wl.dtype == "bf16"
-
-    def conv(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
-    return conv(wl.k_cache), conv(wl.v_cache), torch.from_numpy(wl.page_table).to(device)
+    return synth.device_pages(wl, device)
 
 
 def oracle_inputs(wl):
