@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the same-GPU dense comparison")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp8 256K side measurement")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of sampled oracle attention")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (counter scale reference)")
     return ap.parse_args()
 
 
@@ -258,6 +260,15 @@ def main():
         },
         "extra": extra,
     }
+    if args.calibrate:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(wl, alpha, dense_eq, args.cpu_budget)

@@ -7,7 +7,7 @@
 //   * one workgroup = one (query head, query block of 128 tokens), 4 waves,
 //     each wave owns 32 query rows; two workgroups share a CU;
 //   * the transposed products S^T = K Q^T and O^T = V^T P^T on
-//     v_mfma_f32_32x32x16_bf16 (fp8: v_mfma_f32_32x32x64_f8f6f4), so every
+//     v_mfma_f32_32x32x16_bf16 (fp8 Q K^T: v_mfma_f32_32x32x64_f8f6f4), so every
 //     lane owns ONE query column of S^T and of O^T: the softmax row max/sum
 //     is in-lane plus one v_permlane32_swap, and the O rescale is in-lane;
 //   * the S^T accumulator (keys 8i+4h+j of the lane's query) feeds the P^T
@@ -17,8 +17,11 @@
 //     and K is staged row-major with a 16-byte row pad;
 //   * lists are ascending with the diagonal last, so only the last visited
 //     block needs the causal mask;
-//   * fp32 online softmax in exp2 units, P rounded to bf16 (fp8 path: to
-//     e4m3 after a 2^8 range shift that cancels in the final division).
+//   * fp32 online softmax in exp2 units, P rounded to bf16 for the PV product on
+//     both paths.  The fp8 path keeps Q K^T on the e4m3 MFMA and widens V from
+//     e4m3 to bf16 while staging (exact); rounding P itself to e4m3 (3 mantissa
+//     bits) puts up to 6% error on single weights, which breaks the fp8 error
+//     bound on rows that attend to only a few keys.
 #include "fp_device.h"
 
 namespace fp {
@@ -50,29 +53,24 @@ __device__ inline void transpose8x8_b16(const u32x4 in[8], u32x4 out[8]) {
   }
 }
 
-// 8x8 transpose of bytes: in[e] holds 8 consecutive d (bytes) of key e;
-// out[r] holds key 0..7 of d = r.
-__device__ inline void transpose8x8_b8(const u32x2 in[8], u32x2 out[8]) {
+// 8 e4m3fn codes -> 8 bf16 (exact): decode to fp32 in hardware, keep the top halves.
+__device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
+  u32x4 r;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int w = r >> 2, b = r & 3;
-    // bytes [in0.b, in1.b] into the low half, [in2.b, in3.b] into the high half
-    const unsigned s_lo = (unsigned)b | ((unsigned)(b + 4) << 8) | 0x0c0c0000u;
-    const unsigned s_hi = 0x00000c0cu | ((unsigned)b << 16) | ((unsigned)(b + 4) << 24);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const unsigned lo = __builtin_amdgcn_perm(in[4 * q + 1][w], in[4 * q + 0][w], s_lo);
-      const unsigned hi = __builtin_amdgcn_perm(in[4 * q + 3][w], in[4 * q + 2][w], s_hi);
-      out[r][q] = lo | hi;
-    }
+  for (int w = 0; w < 2; ++w) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
+    r[2 * w] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+    r[2 * w + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
   }
+  return r;
 }
 
 template <int DT, bool PAGED, bool DENSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   constexpr int KP = DT == 0 ? kKPitch16 : kKPitch8;
   constexpr int K_BYTES = kBlock * KP;
-  constexpr int V_BYTES = kBlock * kHeadDim * (DT == 0 ? 2 : 1);
+  constexpr int V_BYTES = kBlock * kHeadDim * 2;  // V is bf16 in LDS on both paths
   __shared__ __attribute__((aligned(16))) unsigned char smem[K_BYTES + V_BYTES];
   unsigned char* Ks = smem;
   unsigned char* Vs = smem + K_BYTES;
@@ -124,7 +122,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 
   float c = a.softmax_scale * kLog2e;  // logits -> log2 units
   if (DT == 1) c *= a.q_scale[h] * a.k_scale[g];
-  const float p_shift = DT == 1 ? 8.0f : 0.0f;  // fp8: P in (0, 256] uses e4m3's range
 
   float m = -__builtin_huge_valf();
   float l = 0.0f;
@@ -190,19 +187,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         const int row = (tid >> 3) + 32 * r;
         kr[r] = row < rows ? *(const u32x4*)(kb + (int64_t)row * a.k_st + (tid & 7) * 16) : zero4();
       }
-      const int c2 = tid >> 7, h2 = (tid >> 6) & 1, r4 = (tid >> 4) & 3, dc = tid & 15;
-      u32x2 vr[8], vt[8];
+      // V: same operand-slot gather as the bf16 path; e4m3 -> bf16 is exact (an e4m3
+      // value has at most 4 significant bits, so the top half of its fp32 is it).
+      const int cc = tid >> 5, h2 = (tid >> 4) & 1, dc = tid & 15;
+      u32x2 vr8[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = 8 * r4 + u;
-        const int key = 32 * (2 * c2 + (e >> 4)) + 8 * ((e & 15) >> 2) + 4 * h2 + (e & 3);
-        vr[u] = key < rows ? *(const u32x2*)(vb + (int64_t)key * a.v_st + dc * 8) : u32x2{0u, 0u};
+      for (int e = 0; e < 8; ++e) {
+        const int key = 16 * cc + 8 * (e >> 2) + 4 * h2 + (e & 3);
+        vr8[e] = key < rows ? *(const u32x2*)(vb + (int64_t)key * a.v_st + dc * 8) : u32x2{0u, 0u};
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) *(u32x4*)(Ks + ((tid >> 3) + 32 * r) * KP + (tid & 7) * 16) = kr[r];
-      transpose8x8_b8(vr, vt);
+      u32x4 vr[8], vt[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) *(u32x2*)(Vs + (((c2 * 2 + h2) * kHeadDim) + 8 * dc + r) * 32 + 8 * r4) = vt[r];
+      for (int e = 0; e < 8; ++e) vr[e] = fp8x8_to_bf16x8(vr8[e]);
+      transpose8x8_b16(vr, vt);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) *(u32x4*)(Vs + (((cc * 2 + h2) * kHeadDim) + 8 * dc + r) * 16) = vt[r];
     }
     __syncthreads();
 
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
     mx = half_swap_max(mx);
     const float mnew = fmaxf(m, mx * c);
     const float alpha = exp2f(m - mnew);
-    const float moff = mnew - p_shift;
+    const float moff = mnew;
     float rs = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -270,39 +271,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
 
-    // ---- O^T += V^T P^T
-    if (DT == 0) {
+    // ---- O^T += V^T P^T (bf16 P and V on both paths)
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const int kt = cc >> 1, t8 = (cc & 1) * 8;
-        bf16x8 pf;
+    for (int cc = 0; cc < 8; ++cc) {
+      const int kt = cc >> 1, t8 = (cc & 1) * 8;
+      bf16x8 pf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[kt][t8 + e];
+      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[kt][t8 + e];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const u32x4 af = *(const u32x4*)(Vs + (((cc * 2 + hh) * kHeadDim) + 32 * dt + ql) * 16);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af), pf, o[dt], 0, 0, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        i32x8 pf;
-#pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) {
-          const int kt = 2 * c2 + (q4 >> 2), v0 = (q4 & 3) * 4;
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kt][v0], sacc[kt][v0 + 1], 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kt][v0 + 2], sacc[kt][v0 + 3], wv, true);
-          pf[q4] = wv;
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const unsigned char* vp = Vs + (((c2 * 2 + hh) * kHeadDim) + 32 * dt + ql) * 32;
-          const u32x4 a0 = *(const u32x4*)vp;
-          const u32x4 a1 = *(const u32x4*)(vp + 16);
-          const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[dt], 0, 0, 0, 0, 0, 0);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        const u32x4 af = *(const u32x4*)(Vs + (((cc * 2 + hh) * kHeadDim) + 32 * dt + ql) * 16);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af), pf, o[dt], 0, 0, 0);
       }
     }
   }
@@ -324,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         *(u32x2*)(orow + (32 * dt + 8 * r + 4 * hh) * 2) = __builtin_bit_cast(u32x2, ov);
       }
     if (a.lse != nullptr && hh == 0) {
-      const float lse = bad ? __builtin_nanf("") : (m - p_shift + log2f(lt)) * kLn2;
+      const float lse = bad ? __builtin_nanf("") : (m + log2f(lt)) * kLn2;
       a.lse[(int64_t)h * p.sd.total_tokens + sp.tok0 + tq] = lse;
     }
   }
