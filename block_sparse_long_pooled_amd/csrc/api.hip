@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstdint>
 #include <string>
 
@@ -241,6 +242,9 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
   }
   if ((r = check_tensor("out", out, FP_BF16, o_st, o_sh))) return r;
   if ((r = check_scales(dtype, q_scale, k_scale, v_scale))) return r;
+  // a 128-token tile is addressed with 32-bit byte offsets from its first row
+  if (k_st * elem_size(dtype) * fp::kBlock > INT32_MAX || v_st * elem_size(dtype) * fp::kBlock > INT32_MAX)
+    return fail(FP_EINVAL, "K/V token stride too large for 32-bit tile offsets");
   if ((idx == nullptr) != (counts == nullptr)) return fail(FP_EINVAL, "idx and counts must both be set or both NULL");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f) return fail(FP_EINVAL, "softmax_scale must be > 0");
   if (lse != nullptr && ((uintptr_t)lse & 3u)) return fail(FP_EINVAL, "lse not 4-byte aligned");

@@ -5,31 +5,36 @@
 //
 // CDNA4 design (not the H20 one on the pages):
 //   * one workgroup = one (query head, query block of 128 tokens), 4 waves,
-//     each wave owns 32 query rows; two workgroups share a CU;
+//     each wave owns 32 query rows; two workgroups share a CU (64 KB LDS each);
 //   * the transposed products S^T = K Q^T and O^T = V^T P^T on
-//     v_mfma_f32_32x32x16_bf16 (fp8 Q K^T: v_mfma_f32_32x32x64_f8f6f4), so every
-//     lane owns ONE query column of S^T and of O^T: the softmax row max/sum
-//     is in-lane plus one v_permlane32_swap, and the O rescale is in-lane;
-//   * the S^T accumulator (keys 8i+4h+j of the lane's query) feeds the P^T
-//     operand of the PV product directly: the contraction over keys only
-//     needs V^T to list keys in the same slot order, so V is staged into LDS
-//     already permuted and transposed (an 8x8 register transpose per thread),
-//     and K is staged row-major with a 16-byte row pad;
-//   * lists are ascending with the diagonal last, so only the last visited
-//     block needs the causal mask;
-//   * fp32 online softmax in exp2 units, P rounded to bf16 for the PV product on
-//     both paths.  The fp8 path keeps Q K^T on the e4m3 MFMA and widens V from
-//     e4m3 to bf16 while staging (exact); rounding P itself to e4m3 (3 mantissa
-//     bits) puts up to 6% error on single weights, which breaks the fp8 error
-//     bound on rows that attend to only a few keys.
+//     v_mfma_f32_32x32x16_bf16 (fp8: v_mfma_f32_32x32x64_f8f6f4), so every
+//     lane owns ONE query column of S^T and of O^T: the softmax row max and sum
+//     are in-lane plus one v_permlane32_swap, and the O rescale is in-lane;
+//   * the S^T accumulator (keys 8i+4h+j of the lane's query) is the P^T
+//     operand of the PV product as it stands: the contraction over keys only
+//     needs V^T to list keys in the same slot order;
+//   * K (and bf16 V) go HBM -> LDS with 16-byte direct loads into rows whose
+//     16-byte chunks are XOR-swizzled by row, so the MFMA operand reads are
+//     free of bank conflicts; bf16 V^T operands come straight from the
+//     row-major tile through ds_read_b64_tr_b16 (transposing LDS reads);
+//   * split-phase pipelining with one K and one V buffer: the loads of tile
+//     n+1's K start as soon as every wave has finished Q K^T of tile n, and
+//     those of its V as soon as P V of tile n is done, so both overlap compute;
+//   * lists are ascending with the diagonal last: only the last visited block
+//     needs the causal mask;
+//   * fp32 online softmax in exp2 units with a lazy rescale: O and the row sum
+//     are rescaled only when the running maximum grows by more than TAU, so P
+//     stays <= 2^TAU; the row sum adds the ROUNDED probabilities, i.e. exactly
+//     the weights that enter P V, so output rows are true convex combinations;
+//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift), V
+//     staged through registers into the operand-slot order with an 8x8 byte
+//     transpose.
 #include "fp_device.h"
 
 namespace fp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKPitch16 = 272;  // bf16 K row in LDS: 256 B + 16 B pad
-constexpr int kKPitch8 = 144;   // fp8 K row in LDS: 128 B + 16 B pad
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -40,41 +45,74 @@ struct AttnK {
   int group;
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// s_waitcnt immediate (gfx9 layout) that waits until at most n vector-memory
+// operations are outstanding and leaves the other counters unconstrained.
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// 8x8 transpose of 16-bit elements: in[e] holds 8 consecutive d of key e;
+// One 16-byte direct HBM -> LDS load per lane; the wave writes 1 KB contiguous
+// at lds_base (wave-uniform) + 16 * lane.
+__device__ inline void dma16(const unsigned char* g, unsigned char* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// 8x8 transpose of bytes: in[e] holds 8 consecutive d (bytes) of key e;
 // out[r] holds key 0..7 of d = r.
-__device__ inline void transpose8x8_b16(const u32x4 in[8], u32x4 out[8]) {
+__device__ inline void transpose8x8_b8(const u32x2 in[8], u32x2 out[8]) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const unsigned sel = (r & 1) ? 0x07060302u : 0x05040100u;
+    const int w = r >> 2, b = r & 3;
+    const unsigned s_lo = (unsigned)b | ((unsigned)(b + 4) << 8) | 0x0c0c0000u;
+    const unsigned s_hi = 0x00000c0cu | ((unsigned)b << 16) | ((unsigned)(b + 4) << 24);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[r][q] = __builtin_amdgcn_perm(in[2 * q + 1][r >> 1], in[2 * q][r >> 1], sel);
+    for (int q = 0; q < 2; ++q) {
+      const unsigned lo = __builtin_amdgcn_perm(in[4 * q + 1][w], in[4 * q + 0][w], s_lo);
+      const unsigned hi = __builtin_amdgcn_perm(in[4 * q + 3][w], in[4 * q + 2][w], s_hi);
+      out[r][q] = lo | hi;
+    }
   }
 }
 
-// 8 e4m3fn codes -> 8 bf16 (exact): decode to fp32 in hardware, keep the top halves.
-__device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
-  u32x4 r;
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], false);
-    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[w], true);
-    r[2 * w] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
-    r[2 * w + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
-  }
-  return r;
+__device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// LDS operand reads.  The restrict-qualified parameter gives each inlined read
+// alias-scope information, which lets the compiler's wait-count pass see that a
+// read of one tile buffer does not depend on the direct loads still filling the
+// other one (otherwise it drains every outstanding load before any LDS read).
+__device__ __attribute__((always_inline)) inline u32x4 lds16(const unsigned char* __restrict__ base, unsigned off) {
+  return *(const u32x4*)(base + off);
+}
+__device__ __attribute__((always_inline)) inline s16x4 lds_tr16(const unsigned char* __restrict__ base, unsigned off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off));
 }
 
-template <int DT, bool PAGED, bool DENSE>
+// Workgroup barrier that does not drain the in-flight HBM -> LDS loads: only
+// this wave's LDS reads/writes must be complete (lgkmcnt), the asm statements
+// keep the compiler from moving memory operations across it.
+__device__ inline void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(15 << 8));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int DT, bool PAGED, bool DENSE, bool LSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
-  constexpr int KP = DT == 0 ? kKPitch16 : kKPitch8;
-  constexpr int K_BYTES = kBlock * KP;
-  constexpr int V_BYTES = kBlock * kHeadDim * 2;  // V is bf16 in LDS on both paths
-  __shared__ __attribute__((aligned(16))) unsigned char smem[K_BYTES + V_BYTES];
-  unsigned char* Ks = smem;
-  unsigned char* Vs = smem + K_BYTES;
-  constexpr int ES = DT == 0 ? 2 : 1;  // element size in bytes
+  constexpr int ES = DT == 0 ? 2 : 1;             // element size in bytes
+  constexpr int KROW = kHeadDim * ES;             // bytes per K (and bf16 V) row
+  constexpr int TILE = kBlock * KROW;             // 32 KB bf16, 16 KB fp8
+  constexpr float TAU = DT == 0 ? 8.0f : 4.0f;    // lazy-rescale slack (log2 units)
+  constexpr float SHIFT = DT == 0 ? 0.0f : 4.0f;  // fp8: P in (0, 2^(TAU+SHIFT)] = (0, 256]
+  constexpr int KLOADS = DT == 0 ? 8 : 4;         // K-tile loads per wave
+  constexpr int VLOADS = 8;                       // V-tile loads per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[TILE];
 
   const AttnLaunch& a = p.a;
   // Work decode: query heads fastest so that consecutive workgroups share the
@@ -98,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = uniform(tid >> 6);
   const int ql = lane & 31;
   const int hh = lane >> 5;
   const int qq = 32 * w + ql;  // query row within the block
@@ -123,119 +161,202 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   float c = a.softmax_scale * kLog2e;  // logits -> log2 units
   if (DT == 1) c *= a.q_scale[h] * a.k_scale[g];
 
-  float m = -__builtin_huge_valf();
-  float l = 0.0f;
-  f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[dt][v] = 0.0f;
-
+  // list entries are wave-uniform: read them through the constant address space
+  // so they become scalar loads (they must not share the vector-memory counter
+  // with the in-flight tile loads).
+  typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
   int cnt;
-  const int32_t* list = nullptr;
+  cint_ptr list = nullptr;
   if (DENSE) {
     cnt = i + 1;
   } else {
-    cnt = a.counts[(int64_t)h * p.sd.total_blocks + sp.blk0 + i];
-    cnt = cnt < 0 ? 0 : (cnt > i + 1 ? i + 1 : cnt);
-    list = a.idx + (int64_t)h * p.sd.total_tri + sp.tri0 + (int64_t)i * (i + 1) / 2;
+    cnt = ((cint_ptr)a.counts)[(int64_t)h * p.sd.total_blocks + sp.blk0 + i];
+    cnt = uniform(cnt < 0 ? 0 : (cnt > i + 1 ? i + 1 : cnt));
+    list = (cint_ptr)(a.idx + (int64_t)h * p.sd.total_tri + sp.tri0 + (int64_t)i * (i + 1) / 2);
   }
   bool bad = cnt == 0;
 
-  for (int n = 0; n < cnt; ++n) {
-    const int j = DENSE ? n : list[n];
-    if (j < 0 || j > i) { bad = true; continue; }
-    const unsigned char* kb;
-    const unsigned char* vb;
+  const unsigned kst = (unsigned)(a.k_st * ES), vst = (unsigned)(a.v_st * ES);  // token strides, bytes
+  // K/V base of list entry n (wave-uniform); an invalid block id or page is
+  // replaced by an in-bounds block (the output of this query block becomes NaN).
+  auto tile = [&](int n, const unsigned char*& kb, const unsigned char*& vb, int& j, int& rows) {
+    j = DENSE ? n : uniform(list[n]);
+    if (j < 0 || j > i) { bad = true; j = 0; }
     if (PAGED) {
-      const int page = p.pd.table[(int64_t)s * p.pd.max_pages + j];
-      if (page < 0 || page >= p.pd.num_pages) { bad = true; continue; }
+      int page = uniform(((cint_ptr)p.pd.table)[(int64_t)s * p.pd.max_pages + j]);
+      if (page < 0 || page >= p.pd.num_pages) { bad = true; page = 0; }
       kb = (const unsigned char*)a.k + ((int64_t)page * a.k_sp + (int64_t)g * a.k_sh) * ES;
       vb = (const unsigned char*)a.v + ((int64_t)page * a.v_sp + (int64_t)g * a.v_sh) * ES;
     } else {
       kb = (const unsigned char*)a.k + ((sp.tok0 + (int64_t)j * kBlock) * a.k_st + (int64_t)g * a.k_sh) * ES;
       vb = (const unsigned char*)a.v + ((sp.tok0 + (int64_t)j * kBlock) * a.v_st + (int64_t)g * a.v_sh) * ES;
     }
-    const int rows = min(kBlock, sp.len - j * kBlock);  // valid key rows of block j
+    rows = min(kBlock, sp.len - j * kBlock);
+  };
 
-    __syncthreads();  // every wave is done reading the previous K/V tile
-    if (DT == 0) {
-      // K: row-major, 16 lanes per 256-byte row, 8 rows per thread
-      u32x4 kr[8];
+  // ---- per-lane byte offsets (the rest of every address is wave-uniform or an
+  //      immediate).  K tile: row R's logical 16-byte chunk c sits at physical
+  //      chunk c ^ (R & 7); bf16 V tile: at c ^ (2 * (R & 3)).
+  // DMA sources: bf16 K needs two variants (R & 7 alternates with the load index).
+  unsigned k_src[2], v_src = 0, k8_src = 0;
+  if (DT == 0) {
+    const int r = lane >> 4, pc = lane & 15;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int row = (tid >> 4) + 16 * r;
-        kr[r] = row < rows ? *(const u32x4*)(kb + (int64_t)row * a.k_st * 2 + (tid & 15) * 16) : zero4();
+    for (int e = 0; e < 2; ++e) k_src[e] = r * kst + ((pc ^ ((r + 4 * e) & 7)) << 4);
+    v_src = r * vst + ((pc ^ (2 * (r & 3))) << 4);
+  } else {
+    const int r = lane >> 3, pc = lane & 7;
+    k8_src = r * kst + ((pc ^ (r & 7)) << 4);
+    k_src[0] = k_src[1] = 0;
+  }
+  // Q K^T operand reads: logical chunk 2st+hh (bf16) of row 32kt+ql; st >= 4 is +128 B.
+  unsigned k_rd[4];
+  if (DT == 0) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) k_rd[st] = ql * KROW + ((((2 * st + hh)) ^ (ql & 7)) << 4);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) k_rd[q] = ql * KROW + (((4 * (q >> 1) + 2 * hh + (q & 1)) ^ (ql & 7)) << 4);
+  }
+  // bf16 V^T transposing reads: source lane sl points at key row 16cc + 8c + 4hh + sl/4,
+  // d = 32dt + 16(G&1) + 4(sl&3); the (dt & 1) bit of the chunk meets the swizzle.
+  unsigned v_rd[2];
+  {
+    const int G = lane >> 4, sl = lane & 15, z = 2 * (sl >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      v_rd[e] = (4 * hh + (sl >> 2)) * KROW + (((4 * e + 2 * (G & 1) + ((sl & 3) >> 1)) ^ z) << 4) + 8 * (sl & 1);
+  }
+  // fp8 V: thread (c2, h2, r4, dc) gathers 8 keys x 8 d of its operand slot group.
+  const int v8_c2 = tid >> 7, v8_h2 = (tid >> 6) & 1, v8_r4 = (tid >> 4) & 3, v8_dc = tid & 15;
+  const unsigned v8_st = (((v8_c2 * 2 + v8_h2) * kHeadDim) + 8 * v8_dc) * 32 + 8 * v8_r4;
+  const unsigned v8_rd = (hh * kHeadDim + ql) * 32;
+
+  auto issue_k = [&](const unsigned char* kb, int rows) {
+    if (rows == kBlock) {
+      if (DT == 0) {
+#pragma unroll
+        for (int u = 0; u < KLOADS; ++u) {
+          const int R0 = 32 * w + 4 * u;
+          dma16(kb + R0 * kst + k_src[u & 1], Ks + R0 * KROW);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < KLOADS; ++u) {
+          const int R0 = 32 * w + 8 * u;
+          dma16(kb + R0 * kst + k8_src, Ks + R0 * KROW);
+        }
       }
-      // V: thread (c, half, d-chunk) gathers the 8 keys of its operand slot group
-      const int cc = tid >> 5, h2 = (tid >> 4) & 1, dc = tid & 15;
-      u32x4 vr[8], vt[8];
+    } else {  // partial last block: rows past the end re-read row 0 (finite, masked)
+      const int per = DT == 0 ? 16 : 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = 16 * cc + 8 * (e >> 2) + 4 * h2 + (e & 3);
-        vr[e] = key < rows ? *(const u32x4*)(vb + (int64_t)key * a.v_st * 2 + dc * 16) : zero4();
+      for (int u = 0; u < KLOADS; ++u) {
+        const int R0 = 32 * w + (DT == 0 ? 4 : 8) * u, R = R0 + lane / per;
+        const int lc = (lane % per) ^ (R & 7);
+        dma16(kb + (R < rows ? R : 0) * kst + (lc << 4), Ks + R0 * KROW);
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) *(u32x4*)(Ks + ((tid >> 4) + 16 * r) * KP + (tid & 15) * 16) = kr[r];
-      transpose8x8_b16(vr, vt);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) *(u32x4*)(Vs + (((cc * 2 + h2) * kHeadDim) + 8 * dc + r) * 16) = vt[r];
-    } else {
-      u32x4 kr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = (tid >> 3) + 32 * r;
-        kr[r] = row < rows ? *(const u32x4*)(kb + (int64_t)row * a.k_st + (tid & 7) * 16) : zero4();
-      }
-      // V: same operand-slot gather as the bf16 path; e4m3 -> bf16 is exact (an e4m3
-      // value has at most 4 significant bits, so the top half of its fp32 is it).
-      const int cc = tid >> 5, h2 = (tid >> 4) & 1, dc = tid & 15;
-      u32x2 vr8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = 16 * cc + 8 * (e >> 2) + 4 * h2 + (e & 3);
-        vr8[e] = key < rows ? *(const u32x2*)(vb + (int64_t)key * a.v_st + dc * 8) : u32x2{0u, 0u};
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x4*)(Ks + ((tid >> 3) + 32 * r) * KP + (tid & 7) * 16) = kr[r];
-      u32x4 vr[8], vt[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vr[e] = fp8x8_to_bf16x8(vr8[e]);
-      transpose8x8_b16(vr, vt);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) *(u32x4*)(Vs + (((cc * 2 + h2) * kHeadDim) + 8 * dc + r) * 16) = vt[r];
     }
-    __syncthreads();
+  };
+  auto issue_v16 = [&](const unsigned char* vb, int rows) {
+    if (rows == kBlock) {
+#pragma unroll
+      for (int u = 0; u < VLOADS; ++u) {
+        const int R0 = 32 * w + 4 * u;
+        dma16(vb + R0 * vst + v_src, Vs + R0 * KROW);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VLOADS; ++u) {
+        const int R0 = 32 * w + 4 * u, R = R0 + (lane >> 4);
+        const int lc = (lane & 15) ^ (2 * (R & 3));
+        dma16(vb + (R < rows ? R : 0) * vst + (lc << 4), Vs + R0 * KROW);
+      }
+    }
+  };
+  u32x2 vreg[8];
+  auto load_v8 = [&](const unsigned char* vb, int rows) {  // rows past the end are zero
+#pragma unroll
+    for (int u = 0; u < VLOADS; ++u) {
+      const int e = 8 * v8_r4 + u;
+      const int key = 32 * (2 * v8_c2 + (e >> 4)) + 8 * ((e & 15) >> 2) + 4 * v8_h2 + (e & 3);
+      vreg[u] = key < rows ? *(const u32x2*)(vb + key * vst + v8_dc * 8) : u32x2{0u, 0u};
+    }
+  };
+  auto store_v8 = [&]() {
+    u32x2 vt[8];
+    transpose8x8_b8(vreg, vt);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) *(u32x2*)(Vs + v8_st + r * 32) = vt[r];
+  };
+
+  float m = -__builtin_huge_valf();  // running reference maximum (log2 units)
+  float l = 0.0f;                    // this lane's half of the row sum (rounded P)
+  float lx = 0.0f;                   // fp8 with LSE: the same sum over unrounded P
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.0f;
+
+  // Q has landed before the tile pipeline starts counting vector-memory ops.
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+
+  const unsigned char *kb = nullptr, *vb = nullptr;
+  int j = 0, rows = 0;
+  if (cnt > 0) {
+    tile(0, kb, vb, j, rows);
+    issue_k(kb, rows);
+    if (DT == 0) issue_v16(vb, rows); else load_v8(vb, rows);
+  }
+
+  for (int n = 0; n < cnt; ++n) {
+    const int jn = j;
+    // K_n has landed once only tile n's V loads can still be outstanding.
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(VLOADS));
+    wg_barrier();
 
     // ---- S^T = K Q^T : 4 tiles of 32 keys x 32 queries per wave
     f32x16 sacc[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.0f;
-      const unsigned char* kp = Ks + (32 * kt + ql) * KP;
-      if (DT == 0) {
+    if (DT == 0) {
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const u32x4 af = *(const u32x4*)(kp + 32 * st + 16 * hh);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
+      for (int st = 0; st < 8; ++st) {
+        u32x4 af[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) af[kt] = lds16(Ks, k_rd[st & 3] + (st >> 2) * 128 + kt * 32 * KROW);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[kt]),
                                                              __builtin_bit_cast(bf16x8, qf[st]), sacc[kt], 0, 0, 0);
-        }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 a0 = *(const u32x4*)(kp + 64 * st + 32 * hh);
-          const u32x4 a1 = *(const u32x4*)(kp + 64 * st + 32 * hh + 16);
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 b0 = qf[2 * st], b1 = qf[2 * st + 1];
+        const i32x8 bf = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const u32x4 a0 = lds16(Ks, k_rd[2 * st] + kt * 32 * KROW);
+          const u32x4 a1 = lds16(Ks, k_rd[2 * st + 1] + kt * 32 * KROW);
           const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          const u32x4 b0 = qf[2 * st], b1 = qf[2 * st + 1];
-          const i32x8 bf = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
           sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, sacc[kt], 0, 0, 0, 0, 0, 0);
         }
       }
     }
+    wg_barrier();  // every wave is done with K_n: its buffer takes K_{n+1}
+
+    const bool more = n + 1 < cnt;
+    if (more) {
+      tile(n + 1, kb, vb, j, rows);
+      issue_k(kb, rows);
+    }
+    if (DT == 1) store_v8();  // V_n: registers -> LDS (the buffer is free since P V of n-1)
 
     // ---- causal mask on the diagonal block (the last list entry)
-    if (j == i) {
+    if (jn == i) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -245,49 +366,99 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         }
     }
 
-    // ---- online softmax (log2 units); each lane holds 64 of its query's 128 keys
+    // ---- online softmax with lazy rescale
     float mx = -__builtin_huge_valf();
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
-    mx = half_swap_max(mx);
-    const float mnew = fmaxf(m, mx * c);
-    const float alpha = exp2f(m - mnew);
-    const float moff = mnew;
-    float rs = 0.0f;
+      for (int v = 0; v < 16; v += 2) mx = max3(mx, sacc[kt][v], sacc[kt][v + 1]);
+    mx = half_swap_max(mx) * c;
+    const bool grow = mx > m + TAU;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? mx : m;
+      const float al = __builtin_amdgcn_exp2f(m - mnew);
+      l *= al;
+      if (DT == 1 && LSE) lx *= al;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = exp2f(fmaf(sacc[kt][v], c, -moff));
-        sacc[kt][v] = pv;
-        rs += pv;
-      }
-    l = l * alpha + rs;
-    m = mnew;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[dt][v] *= al;
+      m = mnew;
+    }
+    const float moff = m - SHIFT;
 
-    // ---- O^T += V^T P^T (bf16 P and V on both paths)
+    // V_n has landed once only tile n+1's K loads can still be outstanding.
+    if (DT == 0) {
+      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_le(KLOADS));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+    }
+    wg_barrier();
+
+    // ---- O^T += V^T P^T, with P formed step by step right before its products.
+    //      The row sum adds exactly the rounded values that enter the product.
+    if (DT == 0) {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int kt = cc >> 1, t8 = (cc & 1) * 8;
-      bf16x8 pf;
+      for (int cc = 0; cc < 8; ++cc) {
+        const int kt = cc >> 1, t8 = (cc & 1) * 8;
+        bf16x8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[kt][t8 + e];
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][t8 + e], c, -moff));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][t8 + e + 1], c, -moff));
+          const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
+          pf[e] = pr[0];
+          pf[e + 1] = pr[1];
+          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const u32x4 af = *(const u32x4*)(Vs + (((cc * 2 + hh) * kHeadDim) + 32 * dt + ql) * 16);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af), pf, o[dt], 0, 0, 0);
+        for (int dt = 0; dt < 4; ++dt) {
+          const unsigned off = v_rd[dt & 1] + (dt >> 1) * 128 + cc * 16 * KROW;
+          const s16x4 t0 = lds_tr16(Vs, off);
+          const s16x4 t1 = lds_tr16(Vs, off + 8 * KROW);
+          const s16x8 af = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af), pf, o[dt], 0, 0, 0);
+        }
       }
+    } else {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        i32x8 pf;
+#pragma unroll
+        for (int q4 = 0; q4 < 8; ++q4) {
+          const int kt = 2 * c2 + (q4 >> 2), v0 = (q4 & 3) * 4;
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v0 + e], c, -moff));
+          if (LSE) lx += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+          wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
+          pf[q4] = wv;
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
+          l += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const unsigned off = v8_rd + c2 * 2 * kHeadDim * 32 + dt * 32 * 32;
+          const u32x4 a0 = lds16(Vs, off);
+          const u32x4 a1 = lds16(Vs, off + 16);
+          const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[dt], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    }
+    wg_barrier();  // every wave is done with V_n: its buffer takes V_{n+1}
+    if (more) {
+      if (DT == 0) issue_v16(vb, rows); else load_v8(vb, rows);
     }
   }
 
   // ---- epilogue: O = O^T / l, bf16 rows of 128 d per query
   const float lt = half_swap_sum(l);
+  // LSE of the exact (unrounded) probabilities; fp8 P is rounded to e4m3 for the
+  // product, so its normaliser lt differs from the exact sum by a few percent.
+  const float lsum = (DT == 1 && LSE) ? half_swap_sum(lx) : lt;
   float inv = 1.0f / lt;
   if (DT == 1) inv *= a.v_scale[g];
   if (bad) inv = __builtin_nanf("");
@@ -302,19 +473,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[dt][4 * r + e] * inv);
         *(u32x2*)(orow + (32 * dt + 8 * r + 4 * hh) * 2) = __builtin_bit_cast(u32x2, ov);
       }
-    if (a.lse != nullptr && hh == 0) {
-      const float lse = bad ? __builtin_nanf("") : (m + log2f(lt)) * kLn2;
+    if (LSE && hh == 0) {
+      const float lse = bad ? __builtin_nanf("") : (m - SHIFT + __builtin_log2f(lsum)) * kLn2;
       a.lse[(int64_t)h * p.sd.total_tokens + sp.tok0 + tq] = lse;
     }
   }
 }
 
+template <int DT, bool PAGED, bool DENSE>
+void launch_l(const AttnK& p, dim3 grid, hipStream_t st) {
+  if (p.a.lse != nullptr)
+    hipLaunchKernelGGL((attn_kernel<DT, PAGED, DENSE, true>), grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<DT, PAGED, DENSE, false>), grid, dim3(kThreads), 0, st, p);
+}
+
 template <int DT, bool PAGED>
 hipError_t launch_t(const AttnK& p, dim3 grid, hipStream_t st) {
-  if (p.a.idx == nullptr)
-    hipLaunchKernelGGL((attn_kernel<DT, PAGED, true>), grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((attn_kernel<DT, PAGED, false>), grid, dim3(kThreads), 0, st, p);
+  if (p.a.idx == nullptr) launch_l<DT, PAGED, true>(p, grid, st);
+  else launch_l<DT, PAGED, false>(p, grid, st);
   return hipGetLastError();
 }
 

@@ -15,6 +15,13 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uniform64(int64_t x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(uint64_t)x);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Where one sequence of a packed batch starts: its first token, its first
 // packed block id and the start of its lists in the triangular-packed idx.
 struct SeqPos {
@@ -48,12 +55,16 @@ __device__ inline SeqPos seq_pos(const SeqDesc& sd, int s) {
     b += __shfl_xor(b, off);
     t += __shfl_xor(t, off);
   }
+  // the butterfly leaves every lane with the same sums: make that visible to the
+  // compiler so everything derived from them lives in scalar registers
+  b = uniform64(b);
+  t = uniform64(t);
   int64_t t0 = sd.cu_seqlens[s];
   int64_t t1 = sd.cu_seqlens[s + 1];
   t0 = t0 < 0 ? 0 : (t0 > sd.total_tokens ? sd.total_tokens : t0);
   t1 = t1 < t0 ? t0 : (t1 > sd.total_tokens ? sd.total_tokens : t1);
-  p.tok0 = t0;
-  p.len = (int)(t1 - t0);
+  p.tok0 = uniform64(t0);
+  p.len = uniform((int)(t1 - t0));
   p.blk0 = b;
   p.tri0 = t;
   return p;
