@@ -47,6 +47,24 @@ def parse():
     return ap.parse_args()
 
 
+def counter_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (already scaled by the copy calibration), or None when the attention
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    prof = os.path.join(root, "profiles", "attn_128k_bf16_hbm_traffic.txt")
+    src = os.path.join(root, "block_sparse_long_pooled_amd", "csrc", "attn.hip")
+    try:
+        fields = dict(line.split(":", 1) for line in open(prof) if ":" in line and not line.startswith("#"))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields["attn_kernel_source_sha256"].strip() != sha:
+            return None
+        return float(fields["attn_traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -256,7 +274,8 @@ def main():
         "roofline": {
             "kernel": "attn_kernel (sparse, bf16)" if wl.dtype == "bf16" else "attn_kernel (sparse, fp8)",
             "bound": "mfma", "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": attn_tflops / peak, "traffic": None,
+            "frac": attn_tflops / peak,
+            "traffic": counter_traffic() if (args.config == 2) else None,
         },
         "extra": extra,
     }
