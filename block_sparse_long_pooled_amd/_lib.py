@@ -10,7 +10,8 @@ import os
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int64, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libflashprefill.so")
+# FLASHPREFILL_LIB selects another build of the same library (e.g. a debug build)
+LIB_PATH = os.environ.get("FLASHPREFILL_LIB") or os.path.join(HERE, "libflashprefill.so")
 
 FP_OK, FP_EINVAL, FP_EUNSUPPORTED, FP_EHIP = 0, 1, 2, 3
 FP_BF16, FP_FP8_E4M3 = 0, 1

@@ -81,6 +81,19 @@ __device__ inline void transpose8x8_b8(const u32x2 in[8], u32x2 out[8]) {
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// Buffer resource over [base, base + nbytes): loads at byte offsets past nbytes
+// return zero, which zero-fills rows past a sequence end without branches.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+// voff is per lane, soff wave-uniform (the instruction's scalar offset).
+__device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ inline u32x2 bload8(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff = 0) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+
 // LDS operand reads.  The restrict-qualified parameter gives each inlined read
 // alias-scope information, which lets the compiler's wait-count pass see that a
 // read of one tile buffer does not depend on the direct loads still filling the
@@ -105,14 +118,19 @@ __device__ inline void wg_barrier() {
 template <int DT, bool PAGED, bool DENSE, bool LSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   constexpr int ES = DT == 0 ? 2 : 1;             // element size in bytes
-  constexpr int KROW = kHeadDim * ES;             // bytes per K (and bf16 V) row
-  constexpr int TILE = kBlock * KROW;             // 32 KB bf16, 16 KB fp8
+  // LDS row pitches (bytes), padded so that the operand reads spread over the 64
+  // LDS banks: K rows of 256 B + 16 (16 consecutive rows hit 16 distinct 16-byte
+  // bank groups), bf16 V rows of 256 B + 64 (the 4-row transposing reads of 64 B
+  // land in 4 disjoint bank quarters), fp8 K rows of 128 B + 16.
+  constexpr int KP = DT == 0 ? 272 : 144;
+  constexpr int VP = 320;
+  constexpr int KT_BYTES = kBlock * KP;
+  constexpr int VT_BYTES = DT == 0 ? kBlock * VP : kBlock * kHeadDim;
   constexpr float TAU = DT == 0 ? 8.0f : 4.0f;    // lazy-rescale slack (log2 units)
   constexpr float SHIFT = DT == 0 ? 0.0f : 4.0f;  // fp8: P in (0, 2^(TAU+SHIFT)] = (0, 256]
-  constexpr int KLOADS = DT == 0 ? 8 : 4;         // K-tile loads per wave
-  constexpr int VLOADS = 8;                       // V-tile loads per wave
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs[TILE];
+  constexpr int KREG = DT == 0 ? 8 : 4;           // 16-byte K loads per thread per tile
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vs[VT_BYTES];
 
   const AttnLaunch& a = p.a;
   // Work decode: query heads fastest so that consecutive workgroups share the
@@ -145,25 +163,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane = query column, 8 (bf16) or
   //      32 (fp8) consecutive d per MFMA step, half hh takes the upper part.
-  const unsigned char* qrow = (const unsigned char*)a.q + ((sp.tok0 + tq) * a.q_st + (int64_t)h * a.q_sh) * ES;
+  // rows of this query block past the sequence end read as zero
+  const int qrows = min(kBlock, sp.len - i * kBlock);
+  const unsigned qst = (unsigned)(a.q_st * ES);
+  const __amdgpu_buffer_rsrc_t qr = rsrc((const unsigned char*)a.q + ((sp.tok0 + (int64_t)i * kBlock) * a.q_st +
+                                                                      (int64_t)h * a.q_sh) * ES, qrows * qst);
   u32x4 qf[DT == 0 ? 8 : 4];
   if (DT == 0) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = qvalid ? *(const u32x4*)(qrow + (16 * st + 8 * hh) * 2) : zero4();
+    for (int st = 0; st < 8; ++st) qf[st] = bload16(qr, qq * qst + (16 * st + 8 * hh) * 2);
   } else {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      qf[2 * st] = qvalid ? *(const u32x4*)(qrow + 64 * st + 32 * hh) : zero4();
-      qf[2 * st + 1] = qvalid ? *(const u32x4*)(qrow + 64 * st + 32 * hh + 16) : zero4();
+      qf[2 * st] = bload16(qr, qq * qst + 64 * st + 32 * hh);
+      qf[2 * st + 1] = bload16(qr, qq * qst + 64 * st + 32 * hh + 16);
     }
   }
+
+  // Q has landed before the tile loads start (the wait-count scoreboard cannot
+  // order these loads against the loop's own loads at the loop header)
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 
   float c = a.softmax_scale * kLog2e;  // logits -> log2 units
   if (DT == 1) c *= a.q_scale[h] * a.k_scale[g];
 
   // list entries are wave-uniform: read them through the constant address space
-  // so they become scalar loads (they must not share the vector-memory counter
-  // with the in-flight tile loads).
+  // so they become scalar loads.
   typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
   int cnt;
   cint_ptr list = nullptr;
@@ -179,8 +204,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   const unsigned kst = (unsigned)(a.k_st * ES), vst = (unsigned)(a.v_st * ES);  // token strides, bytes
   // K/V base of list entry n (wave-uniform); an invalid block id or page is
   // replaced by an in-bounds block (the output of this query block becomes NaN).
-  auto tile = [&](int n, const unsigned char*& kb, const unsigned char*& vb, int& j, int& rows) {
-    j = DENSE ? n : uniform(list[n]);
+  auto tile = [&](int n, const unsigned char*& kb, const unsigned char*& vb, int& rows) -> int {
+    int j = DENSE ? n : uniform(list[n]);
     if (j < 0 || j > i) { bad = true; j = 0; }
     if (PAGED) {
       int page = uniform(((cint_ptr)p.pd.table)[(int64_t)s * p.pd.max_pages + j]);
@@ -192,101 +217,127 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       vb = (const unsigned char*)a.v + ((sp.tok0 + (int64_t)j * kBlock) * a.v_st + (int64_t)g * a.v_sh) * ES;
     }
     rows = min(kBlock, sp.len - j * kBlock);
+    return j;
   };
 
-  // ---- per-lane byte offsets (the rest of every address is wave-uniform or an
-  //      immediate).  K tile: row R's logical 16-byte chunk c sits at physical
-  //      chunk c ^ (R & 7); bf16 V tile: at c ^ (2 * (R & 3)).
-  // DMA sources: bf16 K needs two variants (R & 7 alternates with the load index).
-  unsigned k_src[2], v_src = 0, k8_src = 0;
-  if (DT == 0) {
-    const int r = lane >> 4, pc = lane & 15;
+  // ---- tile staging through registers into padded row-major LDS tiles.  Rows past
+  //      the sequence end read as zero.
+  const int kr_row = DT == 0 ? (tid >> 4) : (tid >> 3);  // first row this thread stages
+  const int kr_chk = DT == 0 ? (tid & 15) : (tid & 7);
+  const unsigned k_ld = kr_row * kst + kr_chk * 16;
+  const unsigned k_sto = kr_row * KP + kr_chk * 16;
+  const unsigned v_ld = (tid >> 4) * vst + (tid & 15) * 16;  // bf16
+  const unsigned v_sto = (tid >> 4) * VP + (tid & 15) * 16;  // bf16
+  constexpr int KSTEP = DT == 0 ? 16 : 32;  // rows between a thread's successive K loads
+  u32x4 kreg[KREG];
+  auto load_k = [&](const unsigned char* kb, int rows) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(kb, rows * kst);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) k_src[e] = r * kst + ((pc ^ ((r + 4 * e) & 7)) << 4);
-    v_src = r * vst + ((pc ^ (2 * (r & 3))) << 4);
-  } else {
-    const int r = lane >> 3, pc = lane & 7;
-    k8_src = r * kst + ((pc ^ (r & 7)) << 4);
-    k_src[0] = k_src[1] = 0;
-  }
-  // Q K^T operand reads: logical chunk 2st+hh (bf16) of row 32kt+ql; st >= 4 is +128 B.
-  unsigned k_rd[4];
-  if (DT == 0) {
+    for (int u = 0; u < KREG; ++u) kreg[u] = bload16(r, k_ld, uniform(u * KSTEP * kst));
+  };
+  auto store_k = [&]() {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) k_rd[st] = ql * KROW + ((((2 * st + hh)) ^ (ql & 7)) << 4);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) k_rd[q] = ql * KROW + (((4 * (q >> 1) + 2 * hh + (q & 1)) ^ (ql & 7)) << 4);
-  }
-  // bf16 V^T transposing reads: source lane sl points at key row 16cc + 8c + 4hh + sl/4,
-  // d = 32dt + 16(G&1) + 4(sl&3); the (dt & 1) bit of the chunk meets the swizzle.
-  unsigned v_rd[2];
-  {
-    const int G = lane >> 4, sl = lane & 15, z = 2 * (sl >> 2);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      v_rd[e] = (4 * hh + (sl >> 2)) * KROW + (((4 * e + 2 * (G & 1) + ((sl & 3) >> 1)) ^ z) << 4) + 8 * (sl & 1);
-  }
-  // fp8 V: thread (c2, h2, r4, dc) gathers 8 keys x 8 d of its operand slot group.
+    for (int u = 0; u < KREG; ++u) *(u32x4*)(Ks + k_sto + u * KSTEP * KP) = kreg[u];
+  };
+  // V: bf16 row-major (8 x 16 B per thread); fp8 gathered per operand slot group
   const int v8_c2 = tid >> 7, v8_h2 = (tid >> 6) & 1, v8_r4 = (tid >> 4) & 3, v8_dc = tid & 15;
-  const unsigned v8_st = (((v8_c2 * 2 + v8_h2) * kHeadDim) + 8 * v8_dc) * 32 + 8 * v8_r4;
-  const unsigned v8_rd = (hh * kHeadDim + ql) * 32;
-
-  auto issue_k = [&](const unsigned char* kb, int rows) {
-    if (rows == kBlock) {
-      if (DT == 0) {
+  // fp8 V operand rows (32 B per (slot group, d)) are split into two 16-byte planes
+  // of 8 KB so each 16-byte operand read of a wave is contiguous.
+  const unsigned v8_st = (v8_r4 >> 1) * 8192 + (((v8_c2 * 2 + v8_h2) * kHeadDim) + 8 * v8_dc) * 16 + 8 * (v8_r4 & 1);
+  u32x4 vreg[DT == 0 ? 8 : 1];
+  u32x2 vreg8[DT == 1 ? 8 : 1];
+  auto load_v = [&](const unsigned char* vb, int rows) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(vb, rows * vst);
+    if (DT == 0) {
 #pragma unroll
-        for (int u = 0; u < KLOADS; ++u) {
-          const int R0 = 32 * w + 4 * u;
-          dma16(kb + R0 * kst + k_src[u & 1], Ks + R0 * KROW);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < KLOADS; ++u) {
-          const int R0 = 32 * w + 8 * u;
-          dma16(kb + R0 * kst + k8_src, Ks + R0 * KROW);
-        }
-      }
-    } else {  // partial last block: rows past the end re-read row 0 (finite, masked)
-      const int per = DT == 0 ? 16 : 8;
-#pragma unroll
-      for (int u = 0; u < KLOADS; ++u) {
-        const int R0 = 32 * w + (DT == 0 ? 4 : 8) * u, R = R0 + lane / per;
-        const int lc = (lane % per) ^ (R & 7);
-        dma16(kb + (R < rows ? R : 0) * kst + (lc << 4), Ks + R0 * KROW);
-      }
-    }
-  };
-  auto issue_v16 = [&](const unsigned char* vb, int rows) {
-    if (rows == kBlock) {
-#pragma unroll
-      for (int u = 0; u < VLOADS; ++u) {
-        const int R0 = 32 * w + 4 * u;
-        dma16(vb + R0 * vst + v_src, Vs + R0 * KROW);
-      }
+      for (int u = 0; u < 8; ++u) vreg[u] = bload16(r, v_ld, uniform(u * 16 * vst));
     } else {
 #pragma unroll
-      for (int u = 0; u < VLOADS; ++u) {
-        const int R0 = 32 * w + 4 * u, R = R0 + (lane >> 4);
-        const int lc = (lane & 15) ^ (2 * (R & 3));
-        dma16(vb + (R < rows ? R : 0) * vst + (lc << 4), Vs + R0 * KROW);
+      for (int u = 0; u < 8; ++u) {
+        const int e = 8 * v8_r4 + u;
+        const int key = 32 * (2 * v8_c2 + (e >> 4)) + 8 * ((e & 15) >> 2) + 4 * v8_h2 + (e & 3);
+        vreg8[u] = bload8(r, key * vst + v8_dc * 8);
       }
     }
   };
-  u32x2 vreg[8];
-  auto load_v8 = [&](const unsigned char* vb, int rows) {  // rows past the end are zero
+  auto store_v = [&]() {
+    if (DT == 0) {
 #pragma unroll
-    for (int u = 0; u < VLOADS; ++u) {
-      const int e = 8 * v8_r4 + u;
-      const int key = 32 * (2 * v8_c2 + (e >> 4)) + 8 * ((e & 15) >> 2) + 4 * v8_h2 + (e & 3);
-      vreg[u] = key < rows ? *(const u32x2*)(vb + key * vst + v8_dc * 8) : u32x2{0u, 0u};
+      for (int u = 0; u < 8; ++u) *(u32x4*)(Vs + v_sto + u * 16 * VP) = vreg[u];
+    } else {
+      u32x2 vt[8];
+      transpose8x8_b8(vreg8, vt);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) *(u32x2*)(Vs + v8_st + r * 16) = vt[r];
     }
   };
-  auto store_v8 = [&]() {
-    u32x2 vt[8];
-    transpose8x8_b8(vreg, vt);
+
+  // ---- operand read offsets (per lane; the rest are immediates)
+  const unsigned k_rd = ql * KP + (DT == 0 ? 16 * hh : 32 * hh);
+  unsigned v_rd;
+  {
+    const int G = lane >> 4, sl = lane & 15;
+    v_rd = (4 * hh + (sl >> 2)) * VP + (16 * (G & 1) + 4 * (sl & 3)) * 2;
+  }
+  const unsigned v8_rd = (hh * kHeadDim + ql) * 16;
+
+  // S^T = K Q^T for one half tile (keys 64*half .. +63): 2 tiles of 32 keys x 32
+  // queries.  The K operands of step st+2 are read while step st's products run, so
+  // every MFMA finds its LDS operand already in registers.
+  auto qk = [&](f32x16 (&sacc)[2], int half) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) *(u32x2*)(Vs + v8_st + r * 32) = vt[r];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[t][v] = 0.0f;
+    const unsigned base = k_rd + 2 * half * 32 * KP;
+    if (DT == 0) {
+      u32x4 af[3][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) af[st][t] = lds16(Ks, base + 32 * st + t * 32 * KP);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st + 2 < 8) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) af[(st + 2) % 3][t] = lds16(Ks, base + 32 * (st + 2) + t * 32 * KP);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[st % 3][t]),
+                                                            __builtin_bit_cast(bf16x8, qf[st]), sacc[t], 0, 0, 0);
+      }
+      // keep the operand reads two steps ahead of their products: 4 reads, then
+      // alternate product / read (the scheduler would otherwise sink each read to
+      // its product and wait out the full LDS latency every time)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < 12; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    } else {
+      u32x4 a0[2][2], a1[2][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          a0[st][t] = lds16(Ks, base + 64 * st + t * 32 * KP);
+          a1[st][t] = lds16(Ks, base + 64 * st + 16 + t * 32 * KP);
+        }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 b0 = qf[2 * st], b1 = qf[2 * st + 1];
+        const i32x8 bf = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 x0 = a0[st][t], x1 = a1[st][t];
+          const i32x8 af = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+          sacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, sacc[t], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    }
   };
 
   float m = -__builtin_huge_valf();  // running reference maximum (log2 units)
@@ -298,80 +349,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.0f;
 
-  // Q has landed before the tile pipeline starts counting vector-memory ops.
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-
-  const unsigned char *kb = nullptr, *vb = nullptr;
-  int j = 0, rows = 0;
-  if (cnt > 0) {
-    tile(0, kb, vb, j, rows);
-    issue_k(kb, rows);
-    if (DT == 0) issue_v16(vb, rows); else load_v8(vb, rows);
-  }
-
-  for (int n = 0; n < cnt; ++n) {
-    const int jn = j;
-    // K_n has landed once only tile n's V loads can still be outstanding.
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(VLOADS));
-    wg_barrier();
-
-    // ---- S^T = K Q^T : 4 tiles of 32 keys x 32 queries per wave
-    f32x16 sacc[4];
+  // online softmax of one half tile of S^T (masked if it belongs to the diagonal
+  // block) and O^T += V^T P^T with the V tile in LDS; P is formed step by step right
+  // before its products and the row sum adds exactly the rounded values that enter
+  // the product.
+  auto softmax_pv = [&](f32x16 (&sacc)[2], int half, bool diag) {
+    if (diag) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.0f;
-    if (DT == 0) {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        u32x4 af[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) af[kt] = lds16(Ks, k_rd[st & 3] + (st >> 2) * 128 + kt * 32 * KROW);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[kt]),
-                                                             __builtin_bit_cast(bf16x8, qf[st]), sacc[kt], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const u32x4 b0 = qf[2 * st], b1 = qf[2 * st + 1];
-        const i32x8 bf = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const u32x4 a0 = lds16(Ks, k_rd[2 * st] + kt * 32 * KROW);
-          const u32x4 a1 = lds16(Ks, k_rd[2 * st + 1] + kt * 32 * KROW);
-          const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, sacc[kt], 0, 0, 0, 0, 0, 0);
-        }
-      }
-    }
-    wg_barrier();  // every wave is done with K_n: its buffer takes K_{n+1}
-
-    const bool more = n + 1 < cnt;
-    if (more) {
-      tile(n + 1, kb, vb, j, rows);
-      issue_k(kb, rows);
-    }
-    if (DT == 1) store_v8();  // V_n: registers -> LDS (the buffer is free since P V of n-1)
-
-    // ---- causal mask on the diagonal block (the last list entry)
-    if (jn == i) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int kk = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (kk > qq) sacc[kt][v] = -__builtin_huge_valf();
+          const int kk = 32 * (2 * half + t) + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (kk > qq) sacc[t][v] = -__builtin_huge_valf();
         }
     }
-
-    // ---- online softmax with lazy rescale
     float mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = max3(mx, sacc[kt][v], sacc[kt][v + 1]);
+      for (int v = 0; v < 16; v += 2) mx = max3(mx, sacc[t][v], sacc[t][v + 1]);
     mx = half_swap_max(mx) * c;
     const bool grow = mx > m + TAU;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -386,26 +382,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       m = mnew;
     }
     const float moff = m - SHIFT;
-
-    // V_n has landed once only tile n+1's K loads can still be outstanding.
-    if (DT == 0) {
-      if (more) __builtin_amdgcn_s_waitcnt(vmcnt_le(KLOADS));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    }
-    wg_barrier();
-
-    // ---- O^T += V^T P^T, with P formed step by step right before its products.
-    //      The row sum adds exactly the rounded values that enter the product.
     if (DT == 0) {
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      // V^T operands of step c4+1 are read while step c4's products run
+      s16x4 vt[2][4][2];
+      auto vread = [&](int buf, int cc) {
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const int kt = cc >> 1, t8 = (cc & 1) * 8;
+        for (int dt = 0; dt < 4; ++dt) {
+          const unsigned off = v_rd + 64 * dt + cc * 16 * VP;
+          vt[buf][dt][0] = lds_tr16(Vs, off);
+          vt[buf][dt][1] = lds_tr16(Vs, off + 8 * VP);
+        }
+      };
+      vread(0, 4 * half);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int cc = 4 * half + c4, t = c4 >> 1, t8 = (c4 & 1) * 8;
+        if (c4 + 1 < 4) vread((c4 + 1) & 1, cc + 1);
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][t8 + e], c, -moff));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][t8 + e + 1], c, -moff));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][t8 + e], c, -moff));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][t8 + e + 1], c, -moff));
           const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
           pf[e] = pr[0];
           pf[e + 1] = pr[1];
@@ -413,44 +411,72 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         }
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const unsigned off = v_rd[dt & 1] + (dt >> 1) * 128 + cc * 16 * KROW;
-          const s16x4 t0 = lds_tr16(Vs, off);
-          const s16x4 t1 = lds_tr16(Vs, off + 8 * KROW);
+          const s16x4 t0 = vt[c4 & 1][dt][0], t1 = vt[c4 & 1][dt][1];
           const s16x8 af = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af), pf, o[dt], 0, 0, 0);
         }
       }
     } else {
+      // one 64-key P^T operand: byte e of half hh <-> key 32*(2*half + e/16) + 8*((e%16)/4) + 4*hh + e%4
+      i32x8 pf;
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        i32x8 pf;
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const int t = q4 >> 2, v0 = (q4 & 3) * 4;
+        float pv[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) {
-          const int kt = 2 * c2 + (q4 >> 2), v0 = (q4 & 3) * 4;
-          float pv[4];
+        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[t][v0 + e], c, -moff));
+        if (LSE) lx += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+        wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
+        pf[q4] = wv;
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
+        l += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+      }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v0 + e], c, -moff));
-          if (LSE) lx += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
-          pf[q4] = wv;
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
-          l += (lo[0] + lo[1]) + (hi[0] + hi[1]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const unsigned off = v8_rd + c2 * 2 * kHeadDim * 32 + dt * 32 * 32;
-          const u32x4 a0 = lds16(Vs, off);
-          const u32x4 a1 = lds16(Vs, off + 16);
-          const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[dt], 0, 0, 0, 0, 0, 0);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        const unsigned off = v8_rd + half * 2 * kHeadDim * 16 + dt * 32 * 16;
+        const u32x4 a0 = lds16(Vs, off);
+        const u32x4 a1 = lds16(Vs, off + 8192);
+        const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[dt], 0, 0, 0, 0, 0, 0);
       }
     }
-    wg_barrier();  // every wave is done with V_n: its buffer takes V_{n+1}
+  };
+
+  // ---- pipeline over the list.  Step n: Q K^T and softmax + P V of the first half
+  //      of tile n, Q K^T of its second half, then the registers take K_{n+1} and
+  //      V_{n+1} while the second half's softmax + P V run; once every wave has
+  //      released both buffers they are rewritten with tile n+1.
+  f32x16 s0[2];
+  if (cnt > 0) {
+    const unsigned char *kb, *vb;
+    int rows;
+    tile(0, kb, vb, rows);
+    load_k(kb, rows);
+    load_v(vb, rows);
+    store_k();
+    store_v();
+  }
+  for (int n = 0; n < cnt; ++n) {
+    const bool more = n + 1 < cnt;
+    const bool diag = !more;   // only the last entry is the diagonal block
+    wg_barrier();              // tile n visible
+    qk(s0, 0);
+    softmax_pv(s0, 0, diag);
+    qk(s0, 1);
     if (more) {
-      if (DT == 0) issue_v16(vb, rows); else load_v8(vb, rows);
+      const unsigned char *kb, *vb;
+      int rows;
+      tile(n + 1, kb, vb, rows);
+      load_k(kb, rows);
+      load_v(vb, rows);
+    }
+    softmax_pv(s0, 1, diag);
+    wg_barrier();              // every wave is done with tile n
+    if (more) {
+      store_k();
+      store_v();
     }
   }
 
