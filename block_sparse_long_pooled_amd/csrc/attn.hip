@@ -26,9 +26,8 @@
 //     are rescaled only when the running maximum grows by more than TAU, so P
 //     stays <= 2^TAU; the row sum adds the ROUNDED probabilities, i.e. exactly
 //     the weights that enter P V, so output rows are true convex combinations;
-//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift), V
-//     staged through registers into the operand-slot order with an 8x8 byte
-//     transpose.
+//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift); V^T
+//     operands come from the row-major tile through ds_read_b64_tr_b8.
 #include "fp_device.h"
 
 namespace fp {
@@ -49,6 +48,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 
 // s_waitcnt immediate (gfx9 layout) that waits until at most n vector-memory
 // operations are outstanding and leaves the other counters unconstrained.
@@ -60,23 +60,6 @@ __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 // at lds_base (wave-uniform) + 16 * lane.
 __device__ inline void dma16(const unsigned char* g, unsigned char* lds_base) {
   __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)lds_base, 16, 0, 0);
-}
-
-// 8x8 transpose of bytes: in[e] holds 8 consecutive d (bytes) of key e;
-// out[r] holds key 0..7 of d = r.
-__device__ inline void transpose8x8_b8(const u32x2 in[8], u32x2 out[8]) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int w = r >> 2, b = r & 3;
-    const unsigned s_lo = (unsigned)b | ((unsigned)(b + 4) << 8) | 0x0c0c0000u;
-    const unsigned s_hi = 0x00000c0cu | ((unsigned)b << 16) | ((unsigned)(b + 4) << 24);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const unsigned lo = __builtin_amdgcn_perm(in[4 * q + 1][w], in[4 * q + 0][w], s_lo);
-      const unsigned hi = __builtin_amdgcn_perm(in[4 * q + 3][w], in[4 * q + 2][w], s_hi);
-      out[r][q] = lo | hi;
-    }
-  }
 }
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -104,6 +87,9 @@ __device__ __attribute__((always_inline)) inline u32x4 lds16(const unsigned char
 __device__ __attribute__((always_inline)) inline s16x4 lds_tr16(const unsigned char* __restrict__ base, unsigned off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off));
 }
+__device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const unsigned char* __restrict__ base, unsigned off) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base + off));
+}
 
 // Workgroup barrier that does not drain the in-flight HBM -> LDS loads: only
 // this wave's LDS reads/writes must be complete (lgkmcnt), the asm statements
@@ -121,11 +107,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   // LDS row pitches (bytes), padded so that the operand reads spread over the 64
   // LDS banks: K rows of 256 B + 16 (16 consecutive rows hit 16 distinct 16-byte
   // bank groups), bf16 V rows of 256 B + 64 (the 4-row transposing reads of 64 B
-  // land in 4 disjoint bank quarters), fp8 K rows of 128 B + 16.
+  // land in 4 disjoint bank quarters), fp8 K and V rows of 128 B + 16 (the 8-row
+  // transposing byte reads hit 8 distinct 16-byte bank groups).
   constexpr int KP = DT == 0 ? 272 : 144;
-  constexpr int VP = 320;
+  constexpr int VP = DT == 0 ? 320 : 144;
   constexpr int KT_BYTES = kBlock * KP;
-  constexpr int VT_BYTES = DT == 0 ? kBlock * VP : kBlock * kHeadDim;
+  constexpr int VT_BYTES = DT == 0 ? kBlock * VP : kBlock * KP;
   constexpr float TAU = DT == 0 ? 8.0f : 4.0f;    // lazy-rescale slack (log2 units)
   constexpr float SHIFT = DT == 0 ? 0.0f : 4.0f;  // fp8: P in (0, 2^(TAU+SHIFT)] = (0, 256]
   constexpr int KREG = DT == 0 ? 8 : 4;           // 16-byte K loads per thread per tile
@@ -227,6 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   const unsigned k_ld = kr_row * kst + kr_chk * 16;
   const unsigned k_sto = kr_row * KP + kr_chk * 16;
   const unsigned v_ld = (tid >> 4) * vst + (tid & 15) * 16;  // bf16
+  const unsigned v8_ld = kr_row * vst + kr_chk * 16;          // fp8 (K geometry)
   const unsigned v_sto = (tid >> 4) * VP + (tid & 15) * 16;  // bf16
   constexpr int KSTEP = DT == 0 ? 16 : 32;  // rows between a thread's successive K loads
   u32x4 kreg[KREG];
@@ -239,13 +227,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 #pragma unroll
     for (int u = 0; u < KREG; ++u) *(u32x4*)(Ks + k_sto + u * KSTEP * KP) = kreg[u];
   };
-  // V: bf16 row-major (8 x 16 B per thread); fp8 gathered per operand slot group
-  const int v8_c2 = tid >> 7, v8_h2 = (tid >> 6) & 1, v8_r4 = (tid >> 4) & 3, v8_dc = tid & 15;
-  // fp8 V operand rows (32 B per (slot group, d)) are split into two 16-byte planes
-  // of 8 KB so each 16-byte operand read of a wave is contiguous.
-  const unsigned v8_st = (v8_r4 >> 1) * 8192 + (((v8_c2 * 2 + v8_h2) * kHeadDim) + 8 * v8_dc) * 16 + 8 * (v8_r4 & 1);
-  u32x4 vreg[DT == 0 ? 8 : 1];
-  u32x2 vreg8[DT == 1 ? 8 : 1];
+  // V: row-major like K (bf16: 8 x 16 B per thread, fp8: 4 x 16 B)
+  u32x4 vreg[KREG];
   auto load_v = [&](const unsigned char* vb, int rows) {
     const __amdgpu_buffer_rsrc_t r = rsrc(vb, rows * vst);
     if (DT == 0) {
@@ -253,11 +236,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       for (int u = 0; u < 8; ++u) vreg[u] = bload16(r, v_ld, uniform(u * 16 * vst));
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = 8 * v8_r4 + u;
-        const int key = 32 * (2 * v8_c2 + (e >> 4)) + 8 * ((e & 15) >> 2) + 4 * v8_h2 + (e & 3);
-        vreg8[u] = bload8(r, key * vst + v8_dc * 8);
-      }
+      for (int u = 0; u < KREG; ++u) vreg[u] = bload16(r, v8_ld, uniform(u * KSTEP * vst));
     }
   };
   auto store_v = [&]() {
@@ -265,10 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) *(u32x4*)(Vs + v_sto + u * 16 * VP) = vreg[u];
     } else {
-      u32x2 vt[8];
-      transpose8x8_b8(vreg8, vt);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) *(u32x2*)(Vs + v8_st + r * 16) = vt[r];
+      for (int u = 0; u < KREG; ++u) *(u32x4*)(Vs + k_sto + u * KSTEP * VP) = vreg[u];
     }
   };
 
@@ -279,7 +256,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
     const int G = lane >> 4, sl = lane & 15;
     v_rd = (4 * hh + (sl >> 2)) * VP + (16 * (G & 1) + 4 * (sl & 3)) * 2;
   }
-  const unsigned v8_rd = (hh * kHeadDim + ql) * 16;
+  // fp8 V^T transposing byte reads (ds_read_b64_tr_b8): within a 16-lane group,
+  // lane i receives byte i&7 of source lanes 2r + i/8 (r = 0..7); source lanes 2r and
+  // 2r+1 point at the same key row, at d0 and d0 + 8, so lane i gets d0 + i for 8
+  // keys.  Byte slot e = 8q + r of half hh holds key 16q + 8(r/4) + 4hh + r%4 (the
+  // P^T operand order), i.e. source lane s reads key row 16q + 8(s/8) + 4hh + (s/2)%4.
+  unsigned v8_rd;
+  {
+    const int G = lane >> 4, sl = lane & 15;
+    v8_rd = (8 * (sl >> 3) + 4 * hh + ((sl >> 1) & 3)) * VP + 16 * (G & 1) + 8 * (sl & 1);
+  }
 
   // S^T = K Q^T for one half tile (keys 64*half .. +63): 2 tiles of 32 keys x 32
   // queries.  The K operands of step st+2 are read while step st's products run, so
@@ -435,10 +421,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const unsigned off = v8_rd + half * 2 * kHeadDim * 16 + dt * 32 * 16;
-        const u32x4 a0 = lds16(Vs, off);
-        const u32x4 a1 = lds16(Vs, off + 8192);
-        const i32x8 af = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        i32x8 af;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 t = lds_tr8(Vs, v8_rd + (64 * half + 16 * q) * VP + 32 * dt);
+          af[2 * q] = t[0];
+          af[2 * q + 1] = t[1];
+        }
         o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, pf, o[dt], 0, 0, 0, 0, 0, 0);
       }
     }
