@@ -4,8 +4,12 @@
 // paged KV cache, continuous batching).
 //
 // CDNA4 design (not the H20 one on the pages):
-//   * one workgroup = one (query head, query block of 128 tokens), 4 waves,
-//     each wave owns 32 query rows; two workgroups share a CU (64 KB LDS each);
+//   * one workgroup = one (query head, query block of 128 tokens), 8 waves and
+//     one workgroup per CU, so the K/V tiles can be double-buffered in LDS
+//     (2 x 74 KB);
+//   * wave w takes query rows 32*(w%4).. +31 against keys 64*(w/4).. +63 of every
+//     tile: the two waves of a row group keep separate online-softmax states over
+//     disjoint key halves and merge them once, after the last tile;
 //   * the transposed products S^T = K Q^T and O^T = V^T P^T on
 //     v_mfma_f32_32x32x16_bf16 (fp8: v_mfma_f32_32x32x64_f8f6f4), so every
 //     lane owns ONE query column of S^T and of O^T: the softmax row max and sum
@@ -13,21 +17,18 @@
 //   * the S^T accumulator (keys 8i+4h+j of the lane's query) is the P^T
 //     operand of the PV product as it stands: the contraction over keys only
 //     needs V^T to list keys in the same slot order;
-//   * K (and bf16 V) go HBM -> LDS with 16-byte direct loads into rows whose
-//     16-byte chunks are XOR-swizzled by row, so the MFMA operand reads are
-//     free of bank conflicts; bf16 V^T operands come straight from the
-//     row-major tile through ds_read_b64_tr_b16 (transposing LDS reads);
-//   * split-phase pipelining with one K and one V buffer: the loads of tile
-//     n+1's K start as soon as every wave has finished Q K^T of tile n, and
-//     those of its V as soon as P V of tile n is done, so both overlap compute;
+//   * K and V travel HBM -> registers -> LDS with 16-byte range-checked buffer
+//     loads issued one tile ahead of their use, and land in padded
+//     row-major tiles whose operand reads are free of bank conflicts; V^T
+//     operands come from the row-major tile through transposing LDS reads
+//     (ds_read_b64_tr_b16, fp8: ds_read_b64_tr_b8);
 //   * lists are ascending with the diagonal last: only the last visited block
 //     needs the causal mask;
 //   * fp32 online softmax in exp2 units with a lazy rescale: O and the row sum
 //     are rescaled only when the running maximum grows by more than TAU, so P
 //     stays <= 2^TAU; the row sum adds the ROUNDED probabilities, i.e. exactly
 //     the weights that enter P V, so output rows are true convex combinations;
-//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift); V^T
-//     operands come from the row-major tile through ds_read_b64_tr_b8.
+//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift).
 #include "fp_device.h"
 
 namespace fp {
@@ -56,12 +57,6 @@ constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | 
 
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// One 16-byte direct HBM -> LDS load per lane; the wave writes 1 KB contiguous
-// at lds_base (wave-uniform) + 16 * lane.
-__device__ inline void dma16(const unsigned char* g, unsigned char* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)lds_base, 16, 0, 0);
-}
-
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Buffer resource over [base, base + nbytes): loads at byte offsets past nbytes
@@ -77,10 +72,7 @@ __device__ inline u32x2 bload8(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
 
-// LDS operand reads.  The restrict-qualified parameter gives each inlined read
-// alias-scope information, which lets the compiler's wait-count pass see that a
-// read of one tile buffer does not depend on the direct loads still filling the
-// other one (otherwise it drains every outstanding load before any LDS read).
+// LDS operand reads (plain, transposing 16-bit, transposing 8-bit).
 __device__ __attribute__((always_inline)) inline u32x4 lds16(const unsigned char* __restrict__ base, unsigned off) {
   return *(const u32x4*)(base + off);
 }
@@ -91,9 +83,9 @@ __device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const unsigned ch
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base + off));
 }
 
-// Workgroup barrier that does not drain the in-flight HBM -> LDS loads: only
-// this wave's LDS reads/writes must be complete (lgkmcnt), the asm statements
-// keep the compiler from moving memory operations across it.
+// Workgroup barrier that does not drain the tile loads in flight: only this
+// wave's LDS reads/writes must be complete (lgkmcnt), the asm statements keep
+// the compiler from moving memory operations across it.
 __device__ inline void wg_barrier() {
   __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(15 << 8));  // lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -104,20 +96,17 @@ __device__ inline void wg_barrier() {
 template <int DT, bool PAGED, bool DENSE, bool LSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   constexpr int ES = DT == 0 ? 2 : 1;             // element size in bytes
-  // LDS row pitches (bytes), padded so that the operand reads spread over the 64
-  // LDS banks: K rows of 256 B + 16 (16 consecutive rows hit 16 distinct 16-byte
-  // bank groups), bf16 V rows of 256 B + 64 (the 4-row transposing reads of 64 B
-  // land in 4 disjoint bank quarters), fp8 K and V rows of 128 B + 16 (the 8-row
-  // transposing byte reads hit 8 distinct 16-byte bank groups).
-  constexpr int KP = DT == 0 ? 272 : 144;
-  constexpr int VP = DT == 0 ? 320 : 144;
-  constexpr int KT_BYTES = kBlock * KP;
-  constexpr int VT_BYTES = DT == 0 ? kBlock * VP : kBlock * KP;
+  constexpr int ROW = kHeadDim * ES;              // bytes of one K/V row: 256 (bf16), 128 (fp8)
+  constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
+  constexpr int HT = 64 * ROW;                    // half tile (64 keys) of K or V: 16 KB / 8 KB
+  constexpr int RPK = 1024 / ROW;                 // rows per 1 KB direct load of one wave
+  constexpr int NI = HT / (1024 * 4);             // direct loads per wave per half tile: 4 / 2
   constexpr float TAU = DT == 0 ? 8.0f : 4.0f;    // lazy-rescale slack (log2 units)
   constexpr float SHIFT = DT == 0 ? 0.0f : 4.0f;  // fp8: P in (0, 2^(TAU+SHIFT)] = (0, 256]
-  constexpr int KREG = DT == 0 ? 8 : 4;           // 16-byte K loads per thread per tile
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[KT_BYTES];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs[VT_BYTES];
+  // Two (K, V) half-tile buffers.  They are separate LDS variables so that the
+  // compiler can tell the direct loads filling one from the operand reads of the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char bufA[2 * HT];
+  __shared__ __attribute__((aligned(1024))) unsigned char bufB[2 * HT];
 
   const AttnLaunch& a = p.a;
   // Work decode: query heads fastest so that consecutive workgroups share the
@@ -167,10 +156,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
     }
   }
 
-  // Q has landed before the tile loads start (the wait-count scoreboard cannot
-  // order these loads against the loop's own loads at the loop header)
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-
   float c = a.softmax_scale * kLog2e;  // logits -> log2 units
   if (DT == 1) c *= a.q_scale[h] * a.k_scale[g];
 
@@ -188,12 +173,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   }
   bool bad = cnt == 0;
 
+  // ---- LDS half tiles: 64 K rows then 64 V rows of ROW bytes, unpadded, with the
+  //      16-byte chunks of every row permuted by an XOR of the row index (swz_k /
+  //      swz_v) so that each operand read below touches every LDS bank at most once
+  //      per cycle.
+  auto swz_k = [](int r) -> int { return DT == 0 ? (r & 15) : ((r >> 1) & 7); };
+  auto swz_v = [](int r) -> int { return DT == 0 ? 4 * (r & 3) : 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1); };
+
+  // ---- direct HBM -> LDS loads of a half tile.  Load u of wave w fills the 1 KB
+  //      at (4u + w) KB of the half: rows RPK*(4u + w) + lane/CPR, physical chunk
+  //      lane%CPR, which holds logical chunk (lane%CPR) ^ swz(row).  The swizzles only
+  //      depend on the lane and on w, so each lane's offset within the 1 KB is the
+  //      same for every u and both halves.  Rows past the sequence end read as zero
+  //      (range check of the buffer resource).
   const unsigned kst = (unsigned)(a.k_st * ES), vst = (unsigned)(a.v_st * ES);  // token strides, bytes
-  // K/V base of list entry n (wave-uniform); an invalid block id or page is
-  // replaced by an in-bounds block (the output of this query block becomes NaN).
-  auto tile = [&](int n, const unsigned char*& kb, const unsigned char*& vb, int& rows) -> int {
-    int j = DENSE ? n : uniform(list[n]);
+  unsigned k_off, v_off;
+  {
+    const int r0 = RPK * w + lane / CPR;  // row of load u = 0; load u adds 4*RPK rows
+    k_off = (lane / CPR) * kst + (((lane % CPR) ^ swz_k(r0)) * 16);
+    v_off = (lane / CPR) * vst + (((lane % CPR) ^ swz_v(r0)) * 16);
+  }
+  auto entry = [&](int n) -> int { return DENSE ? n : uniform(list[n]); };
+  auto load_half = [&](int j, int hf, unsigned char* buf) {
     if (j < 0 || j > i) { bad = true; j = 0; }
+    const unsigned char *kb, *vb;
     if (PAGED) {
       int page = uniform(((cint_ptr)p.pd.table)[(int64_t)s * p.pd.max_pages + j]);
       if (page < 0 || page >= p.pd.num_pages) { bad = true; page = 0; }
@@ -203,90 +206,75 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       kb = (const unsigned char*)a.k + ((sp.tok0 + (int64_t)j * kBlock) * a.k_st + (int64_t)g * a.k_sh) * ES;
       vb = (const unsigned char*)a.v + ((sp.tok0 + (int64_t)j * kBlock) * a.v_st + (int64_t)g * a.v_sh) * ES;
     }
-    rows = min(kBlock, sp.len - j * kBlock);
-    return j;
+    const int rows = min(kBlock, sp.len - j * kBlock);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb, rows * kst);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vb, rows * vst);
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + (4 * u + w) * 1024), 16, k_off,
+                                              uniform((64 * hf + RPK * (4 * u + w)) * kst), 0, 0);
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + HT + (4 * u + w) * 1024), 16, v_off,
+                                              uniform((64 * hf + RPK * (4 * u + w)) * vst), 0, 0);
   };
 
-  // ---- tile staging through registers into padded row-major LDS tiles.  Rows past
-  //      the sequence end read as zero.
-  const int kr_row = DT == 0 ? (tid >> 4) : (tid >> 3);  // first row this thread stages
-  const int kr_chk = DT == 0 ? (tid & 15) : (tid & 7);
-  const unsigned k_ld = kr_row * kst + kr_chk * 16;
-  const unsigned k_sto = kr_row * KP + kr_chk * 16;
-  const unsigned v_ld = (tid >> 4) * vst + (tid & 15) * 16;  // bf16
-  const unsigned v8_ld = kr_row * vst + kr_chk * 16;          // fp8 (K geometry)
-  const unsigned v_sto = (tid >> 4) * VP + (tid & 15) * 16;  // bf16
-  constexpr int KSTEP = DT == 0 ? 16 : 32;  // rows between a thread's successive K loads
-  u32x4 kreg[KREG];
-  auto load_k = [&](const unsigned char* kb, int rows) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(kb, rows * kst);
-#pragma unroll
-    for (int u = 0; u < KREG; ++u) kreg[u] = bload16(r, k_ld, uniform(u * KSTEP * kst));
-  };
-  auto store_k = [&]() {
-#pragma unroll
-    for (int u = 0; u < KREG; ++u) *(u32x4*)(Ks + k_sto + u * KSTEP * KP) = kreg[u];
-  };
-  // V: row-major like K (bf16: 8 x 16 B per thread, fp8: 4 x 16 B)
-  u32x4 vreg[KREG];
-  auto load_v = [&](const unsigned char* vb, int rows) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(vb, rows * vst);
+  // ---- operand read offsets (per lane, loop invariant; rows that differ by a
+  //      multiple of 16 share a swizzle, so row-block steps are immediates)
+  // K operand of step st (bf16: 8 steps of 16 d, fp8: 2 steps of 64 d as 2 x 16 B)
+  unsigned k_rd[DT == 0 ? 8 : 4];
+  {
+    const int r = ql;
     if (DT == 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) vreg[u] = bload16(r, v_ld, uniform(u * 16 * vst));
+      for (int st = 0; st < 8; ++st) k_rd[st] = r * ROW + (((2 * st + hh) ^ swz_k(r)) * 16);
     } else {
 #pragma unroll
-      for (int u = 0; u < KREG; ++u) vreg[u] = bload16(r, v8_ld, uniform(u * KSTEP * vst));
+      for (int e = 0; e < 4; ++e) k_rd[e] = r * ROW + (((4 * (e >> 1) + 2 * hh + (e & 1)) ^ swz_k(r)) * 16);
     }
-  };
-  auto store_v = [&]() {
+  }
+  // V^T operands: bf16 through ds_read_b64_tr_b16 (per 16-lane group G: rows
+  // 4hh + sl/4, 8 bytes at d = 32dt + 16(G&1) + 4(sl&3)); fp8 through
+  // ds_read_b64_tr_b8: within a 16-lane group, lane i receives byte i&7 of source
+  // lanes 2r + i/8 (r = 0..7); source lanes 2r and 2r+1 point at the same key row, at
+  // d0 and d0 + 8, so lane i gets d0 + i for 8 keys.  Byte slot e = 8q + r of half
+  // hh holds key 16q + 8(r/4) + 4hh + r%4 (the P^T operand order), i.e. source lane
+  // s reads key row 16q + 8(s/8) + 4hh + (s/2)%4.
+  unsigned v_rd[4];
+  {
+    const int G = lane >> 4, sl = lane & 15;
     if (DT == 0) {
+      const int r = 4 * hh + (sl >> 2);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) *(u32x4*)(Vs + v_sto + u * 16 * VP) = vreg[u];
+      for (int dt = 0; dt < 4; ++dt)
+        v_rd[dt] = HT + r * ROW + (((4 * dt + 2 * (G & 1) + ((sl & 3) >> 1)) ^ swz_v(r)) * 16) + 8 * (sl & 1);
     } else {
+      const int r = 8 * (sl >> 3) + 4 * hh + ((sl >> 1) & 3);
 #pragma unroll
-      for (int u = 0; u < KREG; ++u) *(u32x4*)(Vs + k_sto + u * KSTEP * VP) = vreg[u];
+      for (int dt = 0; dt < 4; ++dt)
+        v_rd[dt] = HT + r * ROW + (((2 * dt + (G & 1)) ^ swz_v(r)) * 16) + 8 * (sl & 1);
     }
-  };
-
-  // ---- operand read offsets (per lane; the rest are immediates)
-  const unsigned k_rd = ql * KP + (DT == 0 ? 16 * hh : 32 * hh);
-  unsigned v_rd;
-  {
-    const int G = lane >> 4, sl = lane & 15;
-    v_rd = (4 * hh + (sl >> 2)) * VP + (16 * (G & 1) + 4 * (sl & 3)) * 2;
-  }
-  // fp8 V^T transposing byte reads (ds_read_b64_tr_b8): within a 16-lane group,
-  // lane i receives byte i&7 of source lanes 2r + i/8 (r = 0..7); source lanes 2r and
-  // 2r+1 point at the same key row, at d0 and d0 + 8, so lane i gets d0 + i for 8
-  // keys.  Byte slot e = 8q + r of half hh holds key 16q + 8(r/4) + 4hh + r%4 (the
-  // P^T operand order), i.e. source lane s reads key row 16q + 8(s/8) + 4hh + (s/2)%4.
-  unsigned v8_rd;
-  {
-    const int G = lane >> 4, sl = lane & 15;
-    v8_rd = (8 * (sl >> 3) + 4 * hh + ((sl >> 1) & 3)) * VP + 16 * (G & 1) + 8 * (sl & 1);
   }
 
-  // S^T = K Q^T for one half tile (keys 64*half .. +63): 2 tiles of 32 keys x 32
+  // S^T = K Q^T for the 64 keys of the half tile: 2 tiles of 32 keys x 32
   // queries.  The K operands of step st+2 are read while step st's products run, so
   // every MFMA finds its LDS operand already in registers.
-  auto qk = [&](f32x16 (&sacc)[2], int half) {
+  auto qk = [&](f32x16 (&sacc)[2], const unsigned char* buf) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[t][v] = 0.0f;
-    const unsigned base = k_rd + 2 * half * 32 * KP;
     if (DT == 0) {
       u32x4 af[3][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) af[st][t] = lds16(Ks, base + 32 * st + t * 32 * KP);
+        for (int t = 0; t < 2; ++t) af[st][t] = lds16(buf, k_rd[st] + t * 32 * ROW);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         if (st + 2 < 8) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t) af[(st + 2) % 3][t] = lds16(Ks, base + 32 * (st + 2) + t * 32 * KP);
+          for (int t = 0; t < 2; ++t) af[(st + 2) % 3][t] = lds16(buf, k_rd[st + 2] + t * 32 * ROW);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -309,8 +297,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          a0[st][t] = lds16(Ks, base + 64 * st + t * 32 * KP);
-          a1[st][t] = lds16(Ks, base + 64 * st + 16 + t * 32 * KP);
+          a0[st][t] = lds16(buf, k_rd[2 * st] + t * 32 * ROW);
+          a1[st][t] = lds16(buf, k_rd[2 * st + 1] + t * 32 * ROW);
         }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -335,11 +323,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.0f;
 
-  // online softmax of one half tile of S^T (masked if it belongs to the diagonal
-  // block) and O^T += V^T P^T with the V tile in LDS; P is formed step by step right
-  // before its products and the row sum adds exactly the rounded values that enter
-  // the product.
-  auto softmax_pv = [&](f32x16 (&sacc)[2], int half, bool diag) {
+  // online softmax of this wave's 64 keys of S^T (masked if the tile is the
+  // diagonal block) and O^T += V^T P^T with the V tile in LDS; P is formed step by
+  // step right before its products and the row sum adds exactly the rounded values
+  // that enter the product.
+  auto softmax_pv = [&](f32x16 (&sacc)[2], int half, bool diag, const unsigned char* buf) {
     if (diag) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -372,19 +360,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       // V^T operands of step c4+1 are read while step c4's products run
       s16x4 vt[2][4][2];
-      auto vread = [&](int buf, int cc) {
+      auto vread = [&](int vb, int cc) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const unsigned off = v_rd + 64 * dt + cc * 16 * VP;
-          vt[buf][dt][0] = lds_tr16(Vs, off);
-          vt[buf][dt][1] = lds_tr16(Vs, off + 8 * VP);
+          const unsigned off = v_rd[dt] + cc * 16 * ROW;
+          vt[vb][dt][0] = lds_tr16(buf, off);
+          vt[vb][dt][1] = lds_tr16(buf, off + 8 * ROW);
         }
       };
-      vread(0, 4 * half);
+      vread(0, 0);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const int cc = 4 * half + c4, t = c4 >> 1, t8 = (c4 & 1) * 8;
-        if (c4 + 1 < 4) vread((c4 + 1) & 1, cc + 1);
+        const int t = c4 >> 1, t8 = (c4 & 1) * 8;
+        if (c4 + 1 < 4) vread((c4 + 1) & 1, c4 + 1);
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -403,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         }
       }
     } else {
-      // one 64-key P^T operand: byte e of half hh <-> key 32*(2*half + e/16) + 8*((e%16)/4) + 4*hh + e%4
+      // one 64-key P^T operand: byte e of half hh <-> key 64*half + 32*(e/16) + 8*((e%16)/4) + 4*hh + e%4
       i32x8 pf;
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
@@ -424,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
         i32x8 af;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const i32x2 t = lds_tr8(Vs, v8_rd + (64 * half + 16 * q) * VP + 32 * dt);
+          const i32x2 t = lds_tr8(buf, v_rd[dt] + 16 * q * ROW);
           af[2 * q] = t[0];
           af[2 * q + 1] = t[1];
         }
@@ -433,39 +421,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
     }
   };
 
-  // ---- pipeline over the list.  Step n: Q K^T and softmax + P V of the first half
-  //      of tile n, Q K^T of its second half, then the registers take K_{n+1} and
-  //      V_{n+1} while the second half's softmax + P V run; once every wave has
-  //      released both buffers they are rewritten with tile n+1.
+  // ---- pipeline over half tiles.  Half tile (n, 0) sits in buffer A, (n, 1) in
+  //      buffer B.  Each half step waits for its own direct loads, meets the other
+  //      waves at the barrier (past it the half tile is complete and every wave has
+  //      finished the previous half step, i.e. released the other buffer), starts
+  //      the direct loads of the next half tile into the other buffer and computes
+  //      while they fly.  The block id of the next entry is fetched a tile early, so
+  //      the scalar load's latency never sits in front of the tile loads.
   f32x16 s0[2];
   if (cnt > 0) {
-    const unsigned char *kb, *vb;
-    int rows;
-    tile(0, kb, vb, rows);
-    load_k(kb, rows);
-    load_v(vb, rows);
-    store_k();
-    store_v();
-  }
-  for (int n = 0; n < cnt; ++n) {
-    const bool more = n + 1 < cnt;
-    const bool diag = !more;   // only the last entry is the diagonal block
-    wg_barrier();              // tile n visible
-    qk(s0, 0);
-    softmax_pv(s0, 0, diag);
-    qk(s0, 1);
-    if (more) {
-      const unsigned char *kb, *vb;
-      int rows;
-      tile(n + 1, kb, vb, rows);
-      load_k(kb, rows);
-      load_v(vb, rows);
-    }
-    softmax_pv(s0, 1, diag);
-    wg_barrier();              // every wave is done with tile n
-    if (more) {
-      store_k();
-      store_v();
+    int jc = entry(0);
+    int jn = entry(min(1, cnt - 1));
+    load_half(jc, 0, bufA);
+    for (int n = 0; n < cnt; ++n) {
+      const bool diag = n + 1 == cnt;  // only the last entry is the diagonal block
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+      wg_barrier();
+      load_half(jc, 1, bufB);
+      qk(s0, bufA);
+      softmax_pv(s0, 0, diag, bufA);
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+      wg_barrier();
+      if (n + 1 < cnt) load_half(jn, 0, bufA);
+      jc = jn;
+      jn = entry(min(n + 2, cnt - 1));
+      qk(s0, bufB);
+      softmax_pv(s0, 1, diag, bufB);
     }
   }
 
