@@ -93,6 +93,27 @@ def threshold_compact(pooled_q: torch.Tensor, pooled_k: torch.Tensor, alpha: flo
     return idx, counts
 
 
+def mask_words(nb: int) -> int:
+    """32-bit words per row of a bit-packed block mask."""
+    return (nb + 31) // 32
+
+
+def threshold_mask(pooled_q: torch.Tensor, pooled_k: torch.Tensor, alpha: float, n_sink: int, n_local: int,
+                   softmax_scale: Optional[float] = None, mask=None):
+    """The threshold decisions as a bit-packed block mask (int32 words holding uint32
+    bits) [hq, nb, ceil(nb/32)]: bit j%32 of word j//32 of row (h, i) = keep(h, i, j).
+    Words never written are left as allocated (zeros here)."""
+    hq, nb, d = pooled_q.shape
+    hkv = pooled_k.shape[0]
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if mask is None:
+        mask = torch.zeros((hq, nb, mask_words(nb)), dtype=torch.int32, device=pooled_q.device)
+    call("fp_threshold_mask", _ptr(pooled_q), _ptr(pooled_k), nb, hq, hkv, d, float(softmax_scale),
+         float(alpha), int(n_sink), int(n_local), _ptr(mask), _stream(pooled_q))
+    return mask
+
+
 def _attn(name, q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out, return_lse):
     L, hq, d = q.shape
     hkv = k.shape[1]
@@ -106,6 +127,8 @@ def _attn(name, q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, 
             v.stride(0), v.stride(1), out.stride(0), out.stride(1)]
     if name == "fp_sparse_attn":
         args += [_ptr(idx), _ptr(counts)]
+    elif name == "fp_sparse_attn_masked":
+        args += [_ptr(idx)]
     args += [float(softmax_scale), _ptr(out), _ptr(lse), _stream(q)]
     call(name, *args)
     return (out, lse) if return_lse else out
@@ -115,6 +138,15 @@ def sparse_attn(q, k, v, idx, counts, q_scale=None, k_scale=None, v_scale=None, 
                 out=None, return_lse=False):
     """Causal GQA attention of Q [L, hq, 128] over the listed K/V blocks -> bf16 [L, hq, 128]."""
     return _attn("fp_sparse_attn", q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out, return_lse)
+
+
+def sparse_attn_masked(q, k, v, mask, q_scale=None, k_scale=None, v_scale=None, softmax_scale=None,
+                       out=None, return_lse=False):
+    """Logical-skip form of sparse_attn: loops over every causal key block and skips
+    those whose mask bit is 0 (mask from threshold_mask).  Same output as sparse_attn
+    on the lists of the same decisions."""
+    return _attn("fp_sparse_attn_masked", q, k, v, mask, None, q_scale, k_scale, v_scale, softmax_scale, out,
+                 return_lse)
 
 
 def dense_attn(q, k, v, q_scale=None, k_scale=None, v_scale=None, softmax_scale=None, out=None, return_lse=False):

@@ -41,6 +41,10 @@ _SIGNATURES = {
                                _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),
     "fp_dense_attn": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                               _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, c_float, _p, _p, _p]),
+    "fp_mask_words": (c_int, [c_int64]),
+    "fp_threshold_mask": (c_int, [_p, _p, c_int, c_int, c_int, c_int, c_double, c_double, c_int, c_int, _p, _p]),
+    "fp_sparse_attn_masked": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
+                                      _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, c_float, _p, _p, _p]),
     "fp_discover_paged": (c_int, [_p, _p, c_int, _p, _p, _p, c_int, c_int, _i64, _i64, _p, c_int, c_int,
                                   c_int, c_int, c_int, c_int, _i64, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "fp_threshold_compact_varlen": (c_int, [_p, _p, _p, c_int, c_int, _i64, _i64, c_int, c_int, c_int,

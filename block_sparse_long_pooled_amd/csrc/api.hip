@@ -186,9 +186,9 @@ int fp_discover_paged(const void* q, const void* k, int dtype, const float* q_sc
 // ------------------------------------------------------- threshold + compact
 static int select_common(const double* pq, const double* pk, const fp::SeqDesc& sd, int hq, int hkv,
                          double softmax_scale, double alpha, int n_sink, int n_local, int32_t* idx, int32_t* counts,
-                         void* stream) {
+                         void* stream, uint32_t* mask = nullptr) {
   if (pq == nullptr || pk == nullptr) return fail(FP_EINVAL, "pooled input is NULL");
-  if (idx == nullptr || counts == nullptr) return fail(FP_EINVAL, "idx/counts is NULL");
+  if (mask == nullptr && (idx == nullptr || counts == nullptr)) return fail(FP_EINVAL, "idx/counts is NULL");
   if (!std::isfinite(alpha) || alpha < 0.0) return fail(FP_EINVAL, "alpha must be finite and >= 0 (got %g)", alpha);
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0) return fail(FP_EINVAL, "softmax_scale must be > 0");
   if (n_sink < 0) return fail(FP_EINVAL, "n_sink < 0");
@@ -199,7 +199,23 @@ static int select_common(const double* pq, const double* pk, const fp::SeqDesc& 
   a.scale = softmax_scale;
   a.log_alpha = alpha == 0.0 ? -HUGE_VAL : std::log(alpha);
   a.n_sink = n_sink; a.n_local = n_local; a.idx = idx; a.counts = counts;
+  a.mask = mask; a.mask_words = (int)((sd.max_nb + 31) / 32);
   return launch_status(fp::launch_select(a, sd, (hipStream_t)stream));
+}
+
+int fp_mask_words(int64_t nb) { return nb <= 0 ? 0 : (int)((nb + 31) / 32); }
+
+int fp_threshold_mask(const double* pooled_q, const double* pooled_k, int nb, int hq, int hkv, int d,
+                      double softmax_scale, double alpha, int n_sink, int n_local, uint32_t* mask, void* stream) {
+  int r;
+  if ((r = check_shape(FP_BF16, hq, hkv, d, fp::kBlock))) return r;
+  if (nb < 0 || nb > (1 << 24)) return fail(FP_EINVAL, "nb=%d out of range", nb);
+  if (nb == 0) return ok();
+  if (mask == nullptr) return fail(FP_EINVAL, "mask is NULL");
+  if ((uintptr_t)mask & 3u) return fail(FP_EINVAL, "mask not 4-byte aligned");
+  fp::SeqDesc sd = single_seq(nb * fp::kBlock);
+  return select_common(pooled_q, pooled_k, sd, hq, hkv, softmax_scale, alpha, n_sink, n_local, nullptr, nullptr,
+                       stream, mask);
 }
 
 int fp_threshold_compact(const double* pooled_q, const double* pooled_k, int nb, int hq, int hkv, int d,
@@ -231,7 +247,7 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
                        int hq, int hkv, int64_t q_st, int64_t q_sh, int64_t k_sp, int64_t k_st, int64_t k_sh,
                        int64_t v_sp, int64_t v_st, int64_t v_sh, int64_t o_st, int64_t o_sh,
                        const int32_t* idx, const int32_t* counts, float softmax_scale, void* out, float* lse,
-                       void* stream) {
+                       void* stream, const uint32_t* mask = nullptr) {
   int r;
   if ((r = check_tensor("q", q, dtype, q_st, q_sh))) return r;
   if ((r = check_tensor("k", k, dtype, k_st, k_sh))) return r;
@@ -255,7 +271,27 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
   a.q_st = q_st; a.q_sh = q_sh; a.k_sp = k_sp; a.k_st = k_st; a.k_sh = k_sh;
   a.v_sp = v_sp; a.v_st = v_st; a.v_sh = v_sh; a.o_st = o_st; a.o_sh = o_sh;
   a.idx = idx; a.counts = counts; a.softmax_scale = softmax_scale; a.out = out; a.lse = lse;
+  a.mask = mask; a.mask_words = (int)((sd.max_nb + 31) / 32);
   return launch_status(fp::launch_attn(a, sd, pd, (hipStream_t)stream));
+}
+
+int fp_sparse_attn_masked(const void* q, const void* k, const void* v, int dtype,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          int L, int hq, int hkv, int d, int block,
+                          int64_t q_stride_tok, int64_t q_stride_head, int64_t k_stride_tok, int64_t k_stride_head,
+                          int64_t v_stride_tok, int64_t v_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                          const uint32_t* mask, float softmax_scale, void* out, float* lse, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
+  if (L < 0) return fail(FP_EINVAL, "L < 0");
+  if (L == 0) return ok();
+  if (mask == nullptr) return fail(FP_EINVAL, "mask is NULL");
+  if ((uintptr_t)mask & 3u) return fail(FP_EINVAL, "mask not 4-byte aligned");
+  if ((int64_t)hq * nblocks(L) >= (int64_t)1 << 31) return fail(FP_EINVAL, "grid too large");
+  fp::PageDesc pd{nullptr, 0, 0};
+  return attn_common(q, k, v, dtype, q_scale, k_scale, v_scale, single_seq(L), pd, hq, hkv,
+                     q_stride_tok, q_stride_head, 0, k_stride_tok, k_stride_head, 0, v_stride_tok, v_stride_head,
+                     o_stride_tok, o_stride_head, nullptr, nullptr, softmax_scale, out, lse, stream, mask);
 }
 
 int fp_sparse_attn(const void* q, const void* k, const void* v, int dtype,

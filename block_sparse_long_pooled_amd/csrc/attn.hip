@@ -93,7 +93,12 @@ __device__ inline void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int DT, bool PAGED, bool DENSE, bool LSE>
+// MASKED: the logical-skip ablation (FlashPrefill Method 3 contrasts it with
+// physical jumps): the loop visits every causal block j <= i, tests bit j of the
+// row's block mask and branches past unselected blocks.  It cannot start the next
+// selected block's loads before it has found that block, so each selected block
+// waits for its first half tile.
+template <int DT, bool PAGED, bool DENSE, bool LSE, bool MASKED = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   constexpr int ES = DT == 0 ? 2 : 1;             // element size in bytes
   constexpr int ROW = kHeadDim * ES;              // bytes of one K/V row: 256 (bf16), 128 (fp8)
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
   int cnt;
   cint_ptr list = nullptr;
-  if (DENSE) {
+  if (DENSE || MASKED) {
     cnt = i + 1;
   } else {
     cnt = ((cint_ptr)a.counts)[(int64_t)h * p.sd.total_blocks + sp.blk0 + i];
@@ -429,7 +434,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   //      while they fly.  The block id of the next entry is fetched a tile early, so
   //      the scalar load's latency never sits in front of the tile loads.
   f32x16 s0[2];
-  if (cnt > 0) {
+  if (MASKED) {
+    typedef const __attribute__((address_space(4))) uint32_t* cu32_ptr;
+    const cu32_ptr mrow = (cu32_ptr)(a.mask + ((int64_t)h * nb + i) * a.mask_words);
+    unsigned word = 0;
+    int visited = 0;
+    for (int j = 0; j <= i; ++j) {
+      if ((j & 31) == 0) word = uniform(mrow[j >> 5]);
+      if (((word >> (j & 31)) & 1u) == 0) continue;  // logical skip
+      ++visited;
+      load_half(j, 0, bufA);
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+      wg_barrier();  // half 0 in; every wave is done with the previous block's half 1
+      load_half(j, 1, bufB);
+      qk(s0, bufA);
+      softmax_pv(s0, 0, j == i, bufA);
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+      wg_barrier();  // half 1 in; every wave is done with half 0
+      qk(s0, bufB);
+      softmax_pv(s0, 1, j == i, bufB);
+    }
+    bad = visited == 0;
+  } else if (cnt > 0) {
     int jc = entry(0);
     int jn = entry(min(1, cnt - 1));
     load_half(jc, 0, bufA);
@@ -476,6 +502,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   }
 }
 
+template <int DT>
+void launch_masked(const AttnK& p, dim3 grid, hipStream_t st) {
+  if (p.a.lse != nullptr)
+    hipLaunchKernelGGL((attn_kernel<DT, false, false, true, true>), grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_kernel<DT, false, false, false, true>), grid, dim3(kThreads), 0, st, p);
+}
+
 template <int DT, bool PAGED, bool DENSE>
 void launch_l(const AttnK& p, dim3 grid, hipStream_t st) {
   if (p.a.lse != nullptr)
@@ -498,6 +532,11 @@ hipError_t launch_attn(const AttnLaunch& a, const SeqDesc& sd, const PageDesc& p
   const int64_t n_wg = (int64_t)a.hq * sd.max_nb * sd.n_seqs;
   dim3 grid((unsigned)n_wg);
   const bool paged = pd.table != nullptr;
+  if (a.mask != nullptr) {
+    if (a.dtype == 0) launch_masked<0>(p, grid, st);
+    else launch_masked<1>(p, grid, st);
+    return hipGetLastError();
+  }
   if (a.dtype == 0) return paged ? launch_t<0, true>(p, grid, st) : launch_t<0, false>(p, grid, st);
   return paged ? launch_t<1, true>(p, grid, st) : launch_t<1, false>(p, grid, st);
 }

@@ -47,6 +47,8 @@ struct SelectLaunch {
   int n_sink, n_local;
   int32_t* idx;               // [hq, total_tri]
   int32_t* counts;            // [hq, total_blocks]
+  uint32_t* mask;             // bit-packed keep mask [hq, nb, mask_words] instead of lists, or nullptr
+  int mask_words;             // ceil(nb / 32)
 };
 
 struct AttnLaunch {
@@ -63,6 +65,8 @@ struct AttnLaunch {
   float softmax_scale;
   void* out;
   float* lse;                 // [hq, total_tokens] or nullptr
+  const uint32_t* mask;       // logical-skip mode: bit-packed keep mask [hq, nb, mask_words], or nullptr
+  int mask_words;
 };
 
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);

@@ -12,7 +12,9 @@
 // LDS; each thread owns a 4x4 sub-tile.  Compaction: the 16 lanes that share
 // a row hold 4 consecutive columns each, so a 16-lane exclusive prefix sum of
 // the per-lane keep counts gives every kept id its slot, ascending by
-// construction.
+// construction.  The logical-skip ablation asks for the same decisions as a
+// bit-packed block mask instead of lists (32 blocks per word, bit j%32 of word
+// j/32 of row i).
 #include "fp_device.h"
 
 namespace fp {
@@ -63,6 +65,7 @@ __device__ inline void tile_scores(const double* __restrict__ Qb, const double* 
   }
 }
 
+template <bool MASK>
 __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
   const SelectLaunch& a = p.a;
   const int it = blockIdx.x;
@@ -121,6 +124,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
                           ((sc - rmax[x] >= a.log_alpha) || (j < a.n_sink) || (j > i - a.n_local));
         bits |= (keep ? 1u : 0u) << y;
       }
+      if (MASK) {
+        // the 8 lanes tc&~7 .. tc|7 hold the 32 columns of one word of row i
+        unsigned word = bits << (4 * (tc & 7));
+        word |= __shfl_xor(word, 1, 16);
+        word |= __shfl_xor(word, 2, 16);
+        word |= __shfl_xor(word, 4, 16);
+        const int wi = (jt * kTile + tc * 4) >> 5;
+        if ((tc & 7) == 0 && i < nb && wi < a.mask_words) a.mask[((int64_t)h * nb + i) * a.mask_words + wi] = word;
+        continue;
+      }
       const int pc = __popc(bits);
       int incl = pc;
 #pragma unroll
@@ -141,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
       cnt[x] += total;
     }
   }
-  if (tc == 0) {
+  if (!MASK && tc == 0) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int i = row0 + tr * 4 + x;
@@ -156,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st) {
   SelK p{a, sd};
   dim3 grid((sd.max_nb + kTile - 1) / kTile, sd.n_seqs, a.hq);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, st, p);
+  if (a.mask != nullptr) hipLaunchKernelGGL(select_kernel<true>, grid, dim3(kThreads), 0, st, p);
+  else hipLaunchKernelGGL(select_kernel<false>, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -163,6 +163,47 @@ int fp_dense_attn(const void* q, const void* k, const void* v, int dtype,
                   float softmax_scale, void* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Logical-skip ablation.  FlashPrefill Method 3 ("Index Compaction -> Physical
+ * Jumps") contrasts a loop over every block that tests a mask with the compacted
+ * lists the kernel above walks.  These two calls give the mask form of the same
+ * decisions and the masked loop, so the two can be timed side by side.  Single
+ * sequence, packed K/V.
+ *
+ * fp_mask_words -- 32-bit words per mask row: ceil(nb / 32).
+ *
+ * fp_threshold_mask -- the decisions of fp_threshold_compact as a bit-packed
+ *   block mask instead of lists:
+ *   mask   out uint32 [hq, nb, fp_mask_words(nb)], 4-byte aligned; bit (j % 32)
+ *          of word [h, i, j / 32] is keep(h, i, j).  Words that cover some
+ *          j <= i are written (their bits for j > i are 0); the others are not
+ *          touched.
+ *   Other arguments and checks as in fp_threshold_compact.
+ *
+ * fp_sparse_attn_masked -- fp_sparse_attn driven by that mask: the key-block
+ *   loop runs over every j <= i and branches past blocks whose bit is 0, and
+ *   the causal mask applies to block i.  It visits the same blocks in the same
+ *   order as fp_sparse_attn on lists of the same decisions, so the outputs are
+ *   bit-identical.  A row without any set bit gives NaN output.  Other
+ *   arguments as in fp_sparse_attn.
+ * ------------------------------------------------------------------------- */
+int fp_mask_words(int64_t nb);
+
+int fp_threshold_mask(const double* pooled_q, const double* pooled_k,
+                      int nb, int hq, int hkv, int d,
+                      double softmax_scale, double alpha, int n_sink, int n_local,
+                      uint32_t* mask, void* stream);
+
+int fp_sparse_attn_masked(const void* q, const void* k, const void* v, int dtype,
+                          const float* q_scale, const float* k_scale, const float* v_scale,
+                          int L, int hq, int hkv, int d, int block,
+                          int64_t q_stride_tok, int64_t q_stride_head,
+                          int64_t k_stride_tok, int64_t k_stride_head,
+                          int64_t v_stride_tok, int64_t v_stride_head,
+                          int64_t o_stride_tok, int64_t o_stride_head,
+                          const uint32_t* mask, float softmax_scale,
+                          void* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Continuous batching and paged KV (V2 abstract: native paged KV cache and
  * continuous batching).  A batch of n_seqs sequences is packed token-major:
  *

@@ -92,6 +92,8 @@ def attn(name="fp_sparse_attn", **kw):
             a["block"], *a["st"]]
     if name == "fp_sparse_attn":
         args += [a["idx"], a["cnt"]]
+    elif name == "fp_sparse_attn_masked":
+        args += [a["idx"]]
     args += [a["scale"], a["out"], a["lse"], a["stream"]]
     return _lib.status_of(name, *args)
 
@@ -109,6 +111,35 @@ def test_sparse_attn_rejects(kw, code):
 def test_dense_attn_rejects():
     assert attn("fp_dense_attn", out=None) == EINVAL
     assert attn("fp_dense_attn", block=256) == EUNSUP
+
+
+def test_mask_words():
+    lib = _lib.load()
+    assert [lib.fp_mask_words(n) for n in (0, 1, 31, 32, 33, 1024, 2048)] == [0, 1, 1, 1, 2, 32, 64]
+
+
+def mask_select(**kw):
+    a = dict(pq=P, pk=P, nb=32, hq=4, hkv=2, d=128, scale=1 / math.sqrt(128), alpha=0.1, ns=1, nl=2,
+             mask=P, stream=None)
+    a.update(kw)
+    return _lib.status_of("fp_threshold_mask", a["pq"], a["pk"], a["nb"], a["hq"], a["hkv"], a["d"],
+                          a["scale"], a["alpha"], a["ns"], a["nl"], a["mask"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), EINVAL), (dict(mask=P + 2), EINVAL), (dict(alpha=-1.0), EINVAL), (dict(nl=0), EINVAL),
+    (dict(pq=None), EINVAL), (dict(d=64), EUNSUP), (dict(hq=3, hkv=2), EINVAL),
+])
+def test_threshold_mask_rejects(kw, code):
+    assert mask_select(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(idx=None), EINVAL), (dict(idx=P + 2), EINVAL), (dict(out=None), EINVAL), (dict(dtype=1), EINVAL),
+    (dict(block=64), EUNSUP), (dict(scale=0.0), EINVAL),
+])
+def test_sparse_attn_masked_rejects(kw, code):
+    assert attn("fp_sparse_attn_masked", **kw) == code
 
 
 def test_paged_rejects():
@@ -131,3 +162,5 @@ def test_empty_inputs_are_a_no_op():
     assert discover(L=0) == _lib.FP_OK
     assert select(nb=0) == _lib.FP_OK
     assert attn(L=0) == _lib.FP_OK
+    assert mask_select(nb=0) == _lib.FP_OK
+    assert attn("fp_sparse_attn_masked", L=0) == _lib.FP_OK
