@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the same-GPU dense comparison")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp8 256K side measurement")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the logical-skip (masked loop over every block) measurement")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of sampled oracle attention")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter scale reference)")
@@ -121,7 +123,31 @@ def time_hot_path(wl, steps, warmup, alpha):
                attn_ms_min=float(stage[:, 2].min()), sum_counts=int(counts.sum().item()), nb=nb)
     res["counts"] = counts
     res["tensors"] = (q, k, v, qs, ks, vs, out)
+    res["pooled"] = (pq, pk)
     return res
+
+
+def time_logical_skip(r, wl, alpha, reps=2):
+    """The same selection as a bit-packed mask and the masked loop over every causal
+    block (the logical skipping that list compaction replaces)."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    q, k, v, qs, ks, vs, out = r["tensors"]
+    pq, pk = r["pooled"]
+    mask = fp.threshold_mask(pq, pk, alpha, wl.n_sink, wl.n_local)
+    fp.sparse_attn_masked(q, k, v, mask, qs, ks, vs, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        fp.threshold_mask(pq, pk, alpha, wl.n_sink, wl.n_local, mask=mask)
+    ev[1].record()
+    for _ in range(reps):
+        fp.sparse_attn_masked(q, k, v, mask, qs, ks, vs, out=out)
+    ev[2].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
 
 
 def time_dense(tensors, reps=2):
@@ -234,7 +260,15 @@ def main():
         extra["dense_attn_mfma_frac"] = extra["dense_attn_tflops"] / peak
         extra["speedup_vs_dense_step"] = dms / r["ms_per_step"]
         log(f"dense attention {dms:.2f} ms")
-    del r["tensors"]
+    if not args.no_ablation:
+        tm, am = time_logical_skip(r, wl, alpha)
+        extra["logical_skip"] = {
+            "threshold_mask_ms": tm, "attn_ms": am,
+            "physical_jump_speedup": am / r["attn_ms"],
+            "note": "masked loop over every causal block, same selection; outputs bit-identical",
+        }
+        log(f"logical-skip attention {am:.2f} ms (lists: {r['attn_ms']:.2f} ms)")
+    del r["tensors"], r["pooled"]
 
     if not args.no_extra and args.config == 2:
         import torch
@@ -252,7 +286,7 @@ def main():
             "attn_computed_tflops": c8 / (r8["attn_ms"] * 1e-3) / 1e12,
             "mfma_frac_fp8": c8 / (r8["attn_ms"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
         }
-        del r8["tensors"], wl8
+        del r8["tensors"], r8["pooled"], wl8
         log(f"fp8 256K step {extra['fp8_256k']['ms_per_step']:.2f} ms")
 
     line = {
