@@ -36,7 +36,14 @@ it is used):
 * attention is causal inside the diagonal block, softmax scale 1/sqrt(d);
 * varlen/paged: every sequence is processed on its own with queries and keys
   starting at token 0; the page table is addressing only, so it never appears
-  here.
+  here;
+* chunked / prefix-cached prefill (beyond the pages, which only name paged KV
+  and continuous batching for serving): a chunk of len_q queries is the last
+  len_q positions of a sequence whose K/V cache holds len_k tokens; query t sits
+  at position len_k - len_q + t and sees keys up to that position; query blocks
+  follow absolute positions (block I = positions 128I .. 128I+127) and a block's
+  pooled query is the mean of the chunk's tokens in it; the selection of row I
+  is the prefill rule over key blocks 0..I.
 
 Precision: every floating-point step is fp64.  Inputs are the exact values of
 the bf16 bit patterns or of ``e4m3fn_code * scale`` widened to fp64.
@@ -59,6 +66,7 @@ __all__ = [
     "decode_bf16", "decode_e4m3fn", "dequantize", "pool", "block_scores", "reweight",
     "keep_mask", "compact", "select_blocks", "attend_block", "sparse_attention",
     "dense_attention", "select_blocks_varlen", "sparse_attention_varlen", "dense_attention_varlen",
+    "chunk_blocks", "pool_chunk", "select_blocks_chunked", "sparse_attention_chunked",
 ]
 
 
@@ -268,3 +276,86 @@ def sparse_attention_varlen(q, k, v, cu_seqlens, lists_per_seq, block, scale=Non
 def dense_attention_varlen(q, k, v, cu_seqlens, scale=None):
     return np.concatenate([dense_attention(q[a:b], k[a:b], v[a:b], scale)
                            for a, b in _segments(cu_seqlens)], axis=0)
+
+
+# ------------------------------------------------------------ chunked prefill
+def chunk_blocks(len_q: int, len_k: int, block: int):
+    """Absolute query blocks of a chunk of len_q queries ending at position len_k - 1:
+    -> (I0, nq), the first block and the number of blocks the chunk touches."""
+    off = len_k - len_q
+    if len_q == 0:
+        return off // block, 0
+    return off // block, (len_k - 1) // block - off // block + 1
+
+
+def pool_chunk(qc: np.ndarray, len_k: int, block: int) -> np.ndarray:
+    """Pooled query means of a chunk qc [len_q, H, d] whose first query sits at
+    position len_k - len_q: block I averages the chunk's queries at positions
+    128I .. 128I+127 (a block the chunk enters mid-way is averaged over its part).
+    -> [H, nq, d]."""
+    len_q, H, d = qc.shape
+    off = len_k - len_q
+    I0, nq = chunk_blocks(len_q, len_k, block)
+    out = np.empty((H, nq, d), dtype=np.float64)
+    pos = off + np.arange(len_q)
+    for r in range(nq):
+        rows = qc[(pos // block) == I0 + r]
+        out[:, r, :] = rows.sum(axis=0) / rows.shape[0]
+    return out
+
+
+def select_blocks_chunked(qc: np.ndarray, k: np.ndarray, block: int, alpha: float, n_sink: int,
+                          n_local: int, scale: Optional[float] = None) -> Dict[str, object]:
+    """Discovery -> threshold -> compaction for one chunk: row I (absolute query block,
+    I0 <= I < I0 + nq) scores its pooled query against the pooled keys j <= I of the
+    whole cache k [len_k, Hkv, d] and keeps blocks by the prefill rule.  Returns the
+    pooled means, P, keep [hq, nq, nk] (row r = block I0 + r), lists[h][r], counts."""
+    d = qc.shape[-1]
+    len_k = k.shape[0]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    I0, nq = chunk_blocks(qc.shape[0], len_k, block)
+    pq = pool_chunk(qc, len_k, block)
+    pk = pool(k, block)
+    hq, hkv, nk = pq.shape[0], pk.shape[0], pk.shape[1]
+    group = hq // hkv
+    P = np.zeros((hq, nq, nk), dtype=np.float64)
+    keep = np.zeros((hq, nq, nk), dtype=bool)
+    for h in range(hq):
+        for r in range(nq):
+            I = I0 + r
+            s = scale * (pk[h // group, :I + 1] @ pq[h, r])
+            p = np.exp(s - np.max(s))
+            j = np.arange(I + 1)
+            P[h, r, :I + 1] = p
+            keep[h, r, :I + 1] = (p >= alpha) | (j < n_sink) | (j > I - n_local)
+    lists = [[np.nonzero(keep[h, r])[0] for r in range(nq)] for h in range(hq)]
+    counts = keep.sum(axis=-1).astype(np.int64)
+    return dict(pq=pq, pk=pk, P=P, keep=keep, lists=lists, counts=counts, I0=I0, nq=nq)
+
+
+def sparse_attention_chunked(qc: np.ndarray, k: np.ndarray, v: np.ndarray, lists, block: int,
+                             scale: Optional[float] = None, want_lse: bool = False):
+    """Chunk queries qc [len_q, Hq, d] (positions len_k - len_q ..) attend to the cache
+    k, v [len_k, Hkv, d]: query at position p sees keys c <= p whose block is in
+    lists[h][I - I0] for its block I = p // block.  -> O [len_q, Hq, d] (and LSE)."""
+    len_q, hq, d = qc.shape
+    len_k = k.shape[0]
+    group = hq // k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    off = len_k - len_q
+    I0, _ = chunk_blocks(len_q, len_k, block)
+    out = np.empty((len_q, hq, d), dtype=np.float64)
+    lse = np.empty((hq, len_q), dtype=np.float64)
+    for t in range(len_q):
+        p = off + t
+        I = p // block
+        for h in range(hq):
+            g = h // group
+            c = np.concatenate([np.arange(j * block, min((j + 1) * block, len_k)) for j in lists[h][I - I0]])
+            c = c[c <= p]
+            x = scale * (k[c, g, :] @ qc[t, h, :])
+            M = np.max(x)
+            e = np.exp(x - M)
+            out[t, h, :] = (e @ v[c, g, :]) / e.sum()
+            lse[h, t] = M + np.log(e.sum())
+    return (out, lse) if want_lse else out

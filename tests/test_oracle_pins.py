@@ -318,3 +318,107 @@ def test_lse_matches_logsumexp():
     vis = [c for c in range(t + 1) if c // 64 in r["lists"][h][t // 64]]
     x = (q[t, h] @ k[vis, g].T) / math.sqrt(q.shape[-1])
     assert lse[h, t] == pytest.approx(float(torch.logsumexp(torch.from_numpy(x), 0)), rel=1e-13)
+
+
+# ------------------------------------------------------------ chunked prefill
+def test_chunk_blocks_closed_form():
+    """Absolute query blocks a chunk touches, by hand: positions 172..299 lie in
+    blocks 1 and 2; a whole sequence is blocks 0..2; positions 256..299 are block 2
+    alone; an aligned chunk (128..299) starts at its own block; an empty chunk
+    touches none."""
+    assert O.chunk_blocks(128, 300, 128) == (1, 2)
+    assert O.chunk_blocks(300, 300, 128) == (0, 3)
+    assert O.chunk_blocks(44, 300, 128) == (2, 1)
+    assert O.chunk_blocks(172, 300, 128) == (1, 2)
+    assert O.chunk_blocks(0, 300, 128) == (2, 0)
+
+
+def test_pool_chunk_partial_first_block_by_hand():
+    """A chunk entering block 1 at position 150 (len_k 300, len_q 150): block 1
+    averages positions 150..255 only, block 2 positions 256..299 (pure Python)."""
+    qc = rand(150, 2, 3)
+    got = O.pool_chunk(qc, 300, 128)
+    assert got.shape == (2, 2, 3)
+    for h in range(2):
+        for e in range(3):
+            b1 = [qc[t, h, e] for t in range(150) if (150 + t) // 128 == 1]
+            b2 = [qc[t, h, e] for t in range(150) if (150 + t) // 128 == 2]
+            assert len(b1) == 106 and len(b2) == 44
+            assert got[h, 0, e] == pytest.approx(sum(b1) / 106, rel=1e-14, abs=1e-15)
+            assert got[h, 1, e] == pytest.approx(sum(b2) / 44, rel=1e-14, abs=1e-15)
+
+
+def test_chunked_with_whole_sequence_is_prefill():
+    """len_q = len_k: pooled means, lists and outputs equal the prefill functions."""
+    L, block = 5 * 16 + 7, 16
+    q, k, v = rand(L, 4, 8), rand(L, 2, 8), rand(L, 2, 8)
+    a = O.select_blocks_chunked(q, k, block, 0.2, 1, 2)
+    b = O.select_blocks(q, k, block, 0.2, 1, 2)
+    assert np.array_equal(a["pq"], b["pq"])
+    assert np.array_equal(a["counts"], b["counts"])
+    for h in range(4):
+        for i in range(len(b["lists"][h])):
+            assert np.array_equal(a["lists"][h][i], b["lists"][h][i])
+    oa = O.sparse_attention_chunked(q, k, v, a["lists"], block)
+    ob = O.sparse_attention(q, k, v, b["lists"], block)
+    assert np.allclose(oa, ob, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("len_q", [1, 23, 48, 61])
+def test_chunked_dense_equals_tail_of_full_attention(len_q):
+    """All blocks kept: the chunk's outputs and LSE equal the last len_q rows of plain
+    causal attention over the whole sequence (torch fp64 SDPA, bottom-right causal)."""
+    L, block = 3 * 16 + 13, 16
+    q, k, v = rand(L, 4, 8), rand(L, 2, 8), rand(L, 2, 8)
+    sel = O.select_blocks_chunked(q[L - len_q:], k, block, 0.0, 1, 1)
+    assert all(len(lst) == sel["I0"] + r + 1 for h in range(4) for r, lst in enumerate(sel["lists"][h]))
+    out, lse = O.sparse_attention_chunked(q[L - len_q:], k, v, sel["lists"], block, want_lse=True)
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(np.repeat(k, 2, axis=1)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.repeat(v, 2, axis=1)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).permute(1, 0, 2).numpy()
+    assert np.allclose(out, ref[L - len_q:], rtol=1e-10, atol=1e-12)
+    x = (qt @ kt.transpose(1, 2)) / math.sqrt(8)
+    x = x.masked_fill(~torch.ones(L, L, dtype=torch.bool).tril(), float("-inf"))
+    assert np.allclose(lse, torch.logsumexp(x, dim=-1).numpy()[:, L - len_q:], rtol=1e-12, atol=1e-12)
+
+
+def test_block_aligned_chunk_reuses_prefill_rows():
+    """A chunk that starts on a block boundary has the prefill's pooled queries for its
+    blocks, so its lists are the prefill lists of the same rows."""
+    L, block = 6 * 16 + 5, 16
+    q, k = rand(L, 4, 8), rand(L, 2, 8)
+    full = O.select_blocks(q, k, block, 0.15, 1, 2)
+    for start_block in (1, 3, 6):
+        c = O.select_blocks_chunked(q[start_block * block:], k, block, 0.15, 1, 2)
+        assert c["I0"] == start_block
+        for h in range(4):
+            for r in range(c["nq"]):
+                assert np.array_equal(c["lists"][h][r], full["lists"][h][start_block + r])
+
+
+def test_chunked_selection_brute_force():
+    """Tiny chunk starting mid-block: pooled scores, threshold and forced blocks by
+    pure-Python loops."""
+    L, block, d = 5 * 4 + 2, 4, 3
+    len_q = 9
+    q, k = rand(len_q, 2, d), rand(L, 1, d)
+    alpha, n_sink, n_local = 0.3, 1, 2
+    sel = O.select_blocks_chunked(q, k, block, alpha, n_sink, n_local)
+    off = L - len_q
+    nk = -(-L // block)
+    for h in range(2):
+        for r in range(sel["nq"]):
+            I = off // block + r
+            qs = [t for t in range(len_q) if (off + t) // block == I]
+            qbar = [sum(q[t, h, e] for t in qs) / len(qs) for e in range(d)]
+            scores = []
+            for j in range(I + 1):
+                ks = [c for c in range(L) if c // block == j]
+                kbar = [sum(k[c, 0, e] for c in ks) / len(ks) for e in range(d)]
+                scores.append(sum(a * b for a, b in zip(qbar, kbar)) / math.sqrt(d))
+            m = max(scores)
+            want = [j for j in range(I + 1)
+                    if math.exp(scores[j] - m) >= alpha or j < n_sink or j > I - n_local]
+            assert list(sel["lists"][h][r]) == want
+            assert I < nk
