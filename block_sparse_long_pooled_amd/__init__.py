@@ -258,3 +258,118 @@ def sparse_attn_paged(q, k, v, batch: VarlenBatch, idx=None, counts=None, page_t
          q.stride(0), q.stride(1), *ks, *vs, out.stride(0), out.stride(1), _ptr(idx), _ptr(counts),
          float(softmax_scale), _ptr(out), _ptr(lse), _stream(q))
     return (out, lse) if return_lse else out
+
+
+# --------------------------------------------------------------- chunked prefill
+@dataclass
+class ChunkedBatch:
+    """Chunked / prefix-cached prefill batch: sequence s brings q_lengths[s] new
+    queries against a K/V cache of k_lengths[s] >= q_lengths[s] tokens; its queries
+    are the last q_lengths[s] positions.  Query blocks follow absolute positions
+    (block I = positions 128I .. 128I+127), so sequence s has query blocks
+    I0 .. I0+nq-1 with I0 = (k - q) // 128, and list row I has I + 1 slots."""
+    q_lengths: Sequence[int]
+    k_lengths: Sequence[int]
+    device: torch.device
+
+    def __post_init__(self):
+        self.q_lengths = [int(x) for x in self.q_lengths]
+        self.k_lengths = [int(x) for x in self.k_lengths]
+        assert len(self.q_lengths) == len(self.k_lengths)
+        assert all(0 <= q <= k for q, k in zip(self.q_lengths, self.k_lengths)), "need 0 <= len_q <= len_k"
+        cq, ck = [0], [0]
+        for q, k in zip(self.q_lengths, self.k_lengths):
+            cq.append(cq[-1] + q)
+            ck.append(ck[-1] + k)
+        self.cu_seqlens_q = torch.tensor(cq, dtype=torch.int32, device=self.device)
+        self.cu_seqlens_k = torch.tensor(ck, dtype=torch.int32, device=self.device)
+        self.I0, self.nq, self.nk = [], [], []
+        self.cu_qblocks, self.cu_kblocks, self.cu_tri = [0], [0], [0]
+        for q, k in zip(self.q_lengths, self.k_lengths):
+            off = k - q
+            i0 = off // BLOCK
+            nq = (off + q - 1) // BLOCK - i0 + 1 if q > 0 else 0
+            nk = _nb(k)
+            self.I0.append(i0)
+            self.nq.append(nq)
+            self.nk.append(nk)
+            self.cu_qblocks.append(self.cu_qblocks[-1] + nq)
+            self.cu_kblocks.append(self.cu_kblocks[-1] + nk)
+            self.cu_tri.append(self.cu_tri[-1] + nq * (i0 + 1) + nq * (nq - 1) // 2)
+        self.n_seqs = len(self.q_lengths)
+        self.max_seqlen_q = max(self.q_lengths) if self.q_lengths else 0
+        self.max_seqlen_k = max(self.k_lengths) if self.k_lengths else 0
+        self.total_q = cq[-1]
+        self.total_k = ck[-1]
+        self.total_qblocks = self.cu_qblocks[-1]
+        self.total_kblocks = self.cu_kblocks[-1]
+        self.total_tri = self.cu_tri[-1]
+
+    def row_offset(self, s: int, I: int) -> int:
+        """Start of list row (s, absolute query block I) within one head's lists."""
+        r = I - self.I0[s]
+        return self.cu_tri[s] + r * (self.I0[s] + 1) + r * (r - 1) // 2
+
+
+def _kv_strides(k, page_table):
+    if page_table is not None:
+        return k.shape[0], k.shape[2], (k.stride(0), k.stride(1), k.stride(2)), page_table.shape[1]
+    return 0, k.shape[1], (0, k.stride(0), k.stride(1)), 0
+
+
+def discover_chunked(q, k, batch: ChunkedBatch, page_table=None, q_scale=None, k_scale=None,
+                     pooled_q=None, pooled_k=None):
+    """Pooled means of the query blocks of every chunk (absolute block alignment) and
+    of the key blocks of every cache -> (pooled_q [hq, total_qblocks, 128],
+    pooled_k [hkv, total_kblocks, 128]) fp64."""
+    hq, d = q.shape[1], q.shape[2]
+    P, hkv, ks, max_pages = _kv_strides(k, page_table)
+    if pooled_q is None:
+        pooled_q = torch.empty((hq, batch.total_qblocks, d), dtype=torch.float64, device=q.device)
+    if pooled_k is None:
+        pooled_k = torch.empty((hkv, batch.total_kblocks, d), dtype=torch.float64, device=q.device)
+    call("fp_discover_chunked", _ptr(q), _ptr(k), _dtype_code(q), _ptr(q_scale), _ptr(k_scale),
+         _ptr(batch.cu_seqlens_q), _ptr(batch.cu_seqlens_k), batch.n_seqs, batch.max_seqlen_q, batch.max_seqlen_k,
+         batch.total_q, batch.total_k, batch.total_qblocks, batch.total_kblocks, _ptr(page_table), max_pages, P,
+         hq, hkv, d, BLOCK, q.stride(0), q.stride(1), *ks, _ptr(pooled_q), _ptr(pooled_k), _stream(q))
+    return pooled_q, pooled_k
+
+
+def threshold_compact_chunked(pooled_q, pooled_k, batch: ChunkedBatch, alpha: float, n_sink: int, n_local: int,
+                              softmax_scale=None, idx=None, counts=None):
+    """Lists of every (head, sequence, query block) -> (idx [hq * total_tri] int32,
+    counts [hq, total_qblocks] int32); row layout as in ChunkedBatch.row_offset."""
+    hq, _, d = pooled_q.shape
+    hkv = pooled_k.shape[0]
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if idx is None:
+        idx = torch.zeros(hq * batch.total_tri, dtype=torch.int32, device=pooled_q.device)
+    if counts is None:
+        counts = torch.empty((hq, batch.total_qblocks), dtype=torch.int32, device=pooled_q.device)
+    call("fp_threshold_compact_chunked", _ptr(pooled_q), _ptr(pooled_k), _ptr(batch.cu_seqlens_q),
+         _ptr(batch.cu_seqlens_k), batch.n_seqs, batch.max_seqlen_q, batch.max_seqlen_k, batch.total_qblocks,
+         batch.total_kblocks, batch.total_tri, hq, hkv, d, float(softmax_scale), float(alpha), int(n_sink),
+         int(n_local), _ptr(idx), _ptr(counts), _stream(pooled_q))
+    return idx, counts
+
+
+def sparse_attn_chunked(q, k, v, batch: ChunkedBatch, idx=None, counts=None, page_table=None, q_scale=None,
+                        k_scale=None, v_scale=None, softmax_scale=None, out=None, return_lse=False):
+    """Chunk queries attend causally (bottom-right aligned) to their cache over the
+    listed key blocks (idx/counts None = every block) -> bf16 [total_q, hq, 128]."""
+    T, hq, d = q.shape
+    P, hkv, ks, max_pages = _kv_strides(k, page_table)
+    _, _, vs, _ = _kv_strides(v, page_table)
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    call("fp_sparse_attn_chunked", _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(q_scale), _ptr(k_scale),
+         _ptr(v_scale), _ptr(batch.cu_seqlens_q), _ptr(batch.cu_seqlens_k), batch.n_seqs, batch.max_seqlen_q,
+         batch.max_seqlen_k, batch.total_q, batch.total_k, batch.total_qblocks, batch.total_kblocks,
+         batch.total_tri, _ptr(page_table), max_pages, P, hq, hkv, d, BLOCK, q.stride(0), q.stride(1), *ks, *vs,
+         out.stride(0), out.stride(1), _ptr(idx), _ptr(counts), float(softmax_scale), _ptr(out), _ptr(lse),
+         _stream(q))
+    return (out, lse) if return_lse else out

@@ -45,6 +45,16 @@ _SIGNATURES = {
     "fp_threshold_mask": (c_int, [_p, _p, c_int, c_int, c_int, c_int, c_double, c_double, c_int, c_int, _p, _p]),
     "fp_sparse_attn_masked": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                       _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, c_float, _p, _p, _p]),
+    "fp_discover_chunked": (c_int, [_p, _p, c_int, _p, _p, _p, _p, c_int, c_int, c_int, _i64, _i64, _i64, _i64,
+                                    _p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                    _i64, _i64, _i64, _i64, _i64, _p, _p, _p]),
+    "fp_threshold_compact_chunked": (c_int, [_p, _p, _p, _p, c_int, c_int, c_int, _i64, _i64, _i64,
+                                             c_int, c_int, c_int, c_double, c_double, c_int, c_int, _p, _p, _p]),
+    "fp_sparse_attn_chunked": (c_int, [_p, _p, _p, c_int, _p, _p, _p, _p, _p, c_int, c_int, c_int,
+                                       _i64, _i64, _i64, _i64, _i64, _p, c_int, c_int,
+                                       c_int, c_int, c_int, c_int,
+                                       _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       _p, _p, c_float, _p, _p, _p]),
     "fp_discover_paged": (c_int, [_p, _p, c_int, _p, _p, _p, c_int, c_int, _i64, _i64, _p, c_int, c_int,
                                   c_int, c_int, c_int, c_int, _i64, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "fp_threshold_compact_varlen": (c_int, [_p, _p, _p, c_int, c_int, _i64, _i64, c_int, c_int, c_int,

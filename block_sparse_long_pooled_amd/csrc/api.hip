@@ -1,6 +1,7 @@
 // C ABI of libflashprefill (include/flashprefill.h): host-side validation,
 // launch descriptors, status codes.  Nothing here allocates, frees or
 // synchronises; every call only enqueues kernels on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -78,6 +79,10 @@ fp::SeqDesc single_seq(int L) {
   sd.total_tokens = L;
   sd.total_blocks = sd.max_nb;
   sd.total_tri = (int64_t)sd.max_nb * (sd.max_nb + 1) / 2;
+  sd.cu_seqlens_q = nullptr;
+  sd.max_nq = sd.max_nb;
+  sd.total_qtokens = sd.total_tokens;
+  sd.total_qblocks = sd.total_blocks;
   return sd;
 }
 
@@ -96,6 +101,30 @@ int check_varlen(const int32_t* cu, int n_seqs, int max_seqlen, int64_t total_to
   sd->total_tokens = total_tokens;
   sd->total_blocks = total_blocks;
   sd->total_tri = total_tri;
+  sd->cu_seqlens_q = nullptr;
+  sd->max_nq = sd->max_nb;
+  sd->total_qtokens = total_tokens;
+  sd->total_qblocks = total_blocks;
+  return FP_OK;
+}
+
+// Chunked prefill: key (sequence) lengths in cu_k, query lengths in cu_q (each at
+// most the key length; the queries are the last positions of the sequence).
+int check_chunked(const int32_t* cu_q, const int32_t* cu_k, int n_seqs, int max_seqlen_q, int max_seqlen_k,
+                  int64_t total_q, int64_t total_k, int64_t total_qblocks, int64_t total_kblocks, int64_t total_tri,
+                  int hq, fp::SeqDesc* sd) {
+  int r;
+  if (cu_q == nullptr) return fail(FP_EINVAL, "cu_seqlens_q is NULL");
+  if ((r = check_varlen(cu_k, n_seqs, max_seqlen_k, total_k, total_kblocks, total_tri, hq, sd))) return r;
+  if (max_seqlen_q < 0) return fail(FP_EINVAL, "max_seqlen_q < 0");
+  if (total_q < 0 || total_qblocks < 0) return fail(FP_EINVAL, "negative extent");
+  // a chunk of n queries starting mid-block spans at most ceil(n/128) + 1 blocks
+  const int64_t mnq = std::min(nblocks(max_seqlen_q) + (max_seqlen_q > 0 ? 1 : 0), nblocks(max_seqlen_k));
+  if ((int64_t)hq * mnq * n_seqs >= (int64_t)1 << 31) return fail(FP_EINVAL, "grid too large");
+  sd->cu_seqlens_q = cu_q;
+  sd->max_nq = (int)mnq;
+  sd->total_qtokens = total_q;
+  sd->total_qblocks = total_qblocks;
   return FP_OK;
 }
 
@@ -132,10 +161,14 @@ static int discover_common(const void* q, const void* k, int dtype, const float*
   hipStream_t st = (hipStream_t)stream;
   fp::PoolLaunch a{};
   a.dtype = dtype;
+  a.query_view = true;
   a.x = q; a.scale = q_scale; a.H = hq; a.st_page = 0; a.st_tok = q_st; a.st_head = q_sh; a.paged = false;
   a.out = pooled_q;
-  hipError_t e = fp::launch_pool(a, sd, pd, st);
-  if (e != hipSuccess) return launch_status(e);
+  if (sd.max_nq > 0 && sd.total_qblocks > 0) {
+    hipError_t e = fp::launch_pool(a, sd, pd, st);
+    if (e != hipSuccess) return launch_status(e);
+  }
+  a.query_view = false;
   a.x = k; a.scale = k_scale; a.H = hkv; a.st_page = k_sp; a.st_tok = k_st; a.st_head = k_sh;
   a.paged = pd.table != nullptr;
   a.out = pooled_k;
@@ -259,12 +292,13 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
   if ((r = check_tensor("out", out, FP_BF16, o_st, o_sh))) return r;
   if ((r = check_scales(dtype, q_scale, k_scale, v_scale))) return r;
   // a 128-token tile is addressed with 32-bit byte offsets from its first row
-  if (k_st * elem_size(dtype) * fp::kBlock > INT32_MAX || v_st * elem_size(dtype) * fp::kBlock > INT32_MAX)
-    return fail(FP_EINVAL, "K/V token stride too large for 32-bit tile offsets");
+  if (q_st * elem_size(dtype) * fp::kBlock > INT32_MAX || k_st * elem_size(dtype) * fp::kBlock > INT32_MAX ||
+      v_st * elem_size(dtype) * fp::kBlock > INT32_MAX)
+    return fail(FP_EINVAL, "Q/K/V token stride too large for 32-bit tile offsets");
   if ((idx == nullptr) != (counts == nullptr)) return fail(FP_EINVAL, "idx and counts must both be set or both NULL");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f) return fail(FP_EINVAL, "softmax_scale must be > 0");
   if (lse != nullptr && ((uintptr_t)lse & 3u)) return fail(FP_EINVAL, "lse not 4-byte aligned");
-  if (sd.max_nb == 0 || sd.total_tokens == 0) return ok();
+  if (sd.max_nb == 0 || sd.total_tokens == 0 || sd.max_nq == 0 || sd.total_qtokens == 0) return ok();
   fp::AttnLaunch a{};
   a.q = q; a.k = k; a.v = v; a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
   a.dtype = dtype; a.hq = hq; a.hkv = hkv;
@@ -350,6 +384,83 @@ int fp_sparse_attn_paged(const void* q, const void* k, const void* v, int dtype,
   fp::PageDesc pd{page_table, max_pages, num_pages};
   if (page_table != nullptr) {
     if (max_pages < sd.max_nb) return fail(FP_EINVAL, "max_pages=%d < ceil(max_seqlen/128)=%d", max_pages, sd.max_nb);
+    if (num_pages < 1) return fail(FP_EINVAL, "num_pages < 1");
+  }
+  return attn_common(q, k, v, dtype, q_scale, k_scale, v_scale, sd, pd, hq, hkv,
+                     q_stride_tok, q_stride_head, k_stride_page, k_stride_tok, k_stride_head,
+                     v_stride_page, v_stride_tok, v_stride_head, o_stride_tok, o_stride_head,
+                     idx, counts, softmax_scale, out, lse, stream);
+}
+
+// ------------------------------------------------------------ chunked prefill
+int fp_discover_chunked(const void* q, const void* k, int dtype, const float* q_scale, const float* k_scale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seqs,
+                        int max_seqlen_q, int max_seqlen_k, int64_t total_q, int64_t total_k,
+                        int64_t total_qblocks, int64_t total_kblocks,
+                        const int32_t* page_table, int max_pages, int num_pages,
+                        int hq, int hkv, int d, int block,
+                        int64_t q_stride_tok, int64_t q_stride_head,
+                        int64_t k_stride_page, int64_t k_stride_tok, int64_t k_stride_head,
+                        double* pooled_q, double* pooled_k, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
+  fp::SeqDesc sd{};
+  if ((r = check_chunked(cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q, max_seqlen_k, total_q, total_k,
+                         total_qblocks, total_kblocks, 0, hq, &sd))) return r;
+  if (total_k == 0 || sd.max_nb == 0) return ok();
+  if ((r = check_tensor("q", q, dtype, q_stride_tok, q_stride_head))) return r;
+  if ((r = check_tensor("k", k, dtype, k_stride_tok, k_stride_head))) return r;
+  fp::PageDesc pd{page_table, max_pages, num_pages};
+  if (page_table != nullptr) {
+    if ((r = check_tensor("k", k, dtype, k_stride_page, 0))) return r;
+    if (max_pages < sd.max_nb) return fail(FP_EINVAL, "max_pages=%d < ceil(max_seqlen_k/128)=%d", max_pages, sd.max_nb);
+    if (num_pages < 1) return fail(FP_EINVAL, "num_pages < 1");
+  }
+  if (dtype == FP_FP8_E4M3 && (q_scale == nullptr || k_scale == nullptr)) return fail(FP_EINVAL, "fp8 needs q/k scales");
+  return discover_common(q, k, dtype, q_scale, k_scale, sd, pd, hq, hkv, q_stride_tok, q_stride_head,
+                         k_stride_page, k_stride_tok, k_stride_head, pooled_q, pooled_k, stream);
+}
+
+int fp_threshold_compact_chunked(const double* pooled_q, const double* pooled_k,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seqs,
+                                 int max_seqlen_q, int max_seqlen_k, int64_t total_qblocks, int64_t total_kblocks,
+                                 int64_t total_tri, int hq, int hkv, int d,
+                                 double softmax_scale, double alpha, int n_sink, int n_local,
+                                 int32_t* idx, int32_t* counts, void* stream) {
+  int r;
+  if ((r = check_shape(FP_BF16, hq, hkv, d, fp::kBlock))) return r;
+  fp::SeqDesc sd{};
+  if ((r = check_chunked(cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q, max_seqlen_k, 0, 0, total_qblocks,
+                         total_kblocks, total_tri, hq, &sd))) return r;
+  // lengths only; no token buffer is touched here
+  sd.total_tokens = (int64_t)1 << 62;
+  sd.total_qtokens = (int64_t)1 << 62;
+  if (sd.max_nq == 0 || total_qblocks == 0) return ok();
+  return select_common(pooled_q, pooled_k, sd, hq, hkv, softmax_scale, alpha, n_sink, n_local, idx, counts, stream);
+}
+
+int fp_sparse_attn_chunked(const void* q, const void* k, const void* v, int dtype,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seqs,
+                           int max_seqlen_q, int max_seqlen_k, int64_t total_q, int64_t total_k,
+                           int64_t total_qblocks, int64_t total_kblocks, int64_t total_tri,
+                           const int32_t* page_table, int max_pages, int num_pages,
+                           int hq, int hkv, int d, int block,
+                           int64_t q_stride_tok, int64_t q_stride_head,
+                           int64_t k_stride_page, int64_t k_stride_tok, int64_t k_stride_head,
+                           int64_t v_stride_page, int64_t v_stride_tok, int64_t v_stride_head,
+                           int64_t o_stride_tok, int64_t o_stride_head,
+                           const int32_t* idx, const int32_t* counts, float softmax_scale,
+                           void* out, float* lse, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
+  fp::SeqDesc sd{};
+  if ((r = check_chunked(cu_seqlens_q, cu_seqlens_k, n_seqs, max_seqlen_q, max_seqlen_k, total_q, total_k,
+                         total_qblocks, total_kblocks, total_tri, hq, &sd))) return r;
+  if (total_q == 0 || total_k == 0 || sd.max_nq == 0) return ok();
+  fp::PageDesc pd{page_table, max_pages, num_pages};
+  if (page_table != nullptr) {
+    if (max_pages < sd.max_nb) return fail(FP_EINVAL, "max_pages=%d < ceil(max_seqlen_k/128)=%d", max_pages, sd.max_nb);
     if (num_pages < 1) return fail(FP_EINVAL, "num_pages < 1");
   }
   return attn_common(q, k, v, dtype, q_scale, k_scale, v_scale, sd, pd, hq, hkv,

@@ -127,10 +127,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   }
   const int rest = id / a.hq;
   const int s = rest % p.sd.n_seqs;
-  const int i = p.sd.max_nb - 1 - rest / p.sd.n_seqs;  // heaviest query blocks first
+  const int r = p.sd.max_nq - 1 - rest / p.sd.n_seqs;  // heaviest query blocks first
   const SeqPos sp = seq_pos(p.sd, s);
-  const int nb = (sp.len + kBlock - 1) / kBlock;
-  if (i < 0 || i >= nb || sp.blk0 + i >= p.sd.total_blocks) return;
+  if (r < 0 || r >= sp.nq || sp.qblk0 + r >= p.sd.total_qblocks) return;
+  // query block r of the sequence is absolute block i: its rows are positions
+  // 128i .. 128i+127, of which the query chunk holds [qoff, qoff + qlen)
+  const int i = sp.I0 + r;
   const int g = h / p.group;
 
   const int tid = threadIdx.x;
@@ -138,26 +140,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   const int w = uniform(tid >> 6);
   const int ql = lane & 31;
   const int hh = lane >> 5;
-  const int qq = 32 * w + ql;  // query row within the block
-  const int tq = i * kBlock + qq;
-  const bool qvalid = tq < sp.len;
+  const int qq = 32 * w + ql;  // query row within the block (= position - 128i)
+  const int tq = i * kBlock + qq - sp.qoff;  // index of the row in the query chunk
+  const bool qvalid = tq >= 0 && tq < sp.qlen;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane = query column, 8 (bf16) or
   //      32 (fp8) consecutive d per MFMA step, half hh takes the upper part.
-  // rows of this query block past the sequence end read as zero
-  const int qrows = min(kBlock, sp.len - i * kBlock);
+  // The resource starts at the block's first row the chunk holds (row qs0 of the
+  // block); rows before it (negative offsets wrap) and past the chunk end are out
+  // of range and read as zero.
+  const int qs0 = max(0, sp.qoff - i * kBlock);
+  const int qrows = min(kBlock, sp.qoff + sp.qlen - i * kBlock) - qs0;
   const unsigned qst = (unsigned)(a.q_st * ES);
-  const __amdgpu_buffer_rsrc_t qr = rsrc((const unsigned char*)a.q + ((sp.tok0 + (int64_t)i * kBlock) * a.q_st +
-                                                                      (int64_t)h * a.q_sh) * ES, qrows * qst);
+  const __amdgpu_buffer_rsrc_t qr =
+      rsrc((const unsigned char*)a.q + ((sp.qtok0 + (int64_t)i * kBlock + qs0 - sp.qoff) * a.q_st +
+                                        (int64_t)h * a.q_sh) * ES, qrows * qst);
+  const unsigned qro = (unsigned)(qq - qs0) * qst;
   u32x4 qf[DT == 0 ? 8 : 4];
   if (DT == 0) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qf[st] = bload16(qr, qq * qst + (16 * st + 8 * hh) * 2);
+    for (int st = 0; st < 8; ++st) qf[st] = bload16(qr, qro + (16 * st + 8 * hh) * 2);
   } else {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      qf[2 * st] = bload16(qr, qq * qst + 64 * st + 32 * hh);
-      qf[2 * st + 1] = bload16(qr, qq * qst + 64 * st + 32 * hh + 16);
+      qf[2 * st] = bload16(qr, qro + 64 * st + 32 * hh);
+      qf[2 * st + 1] = bload16(qr, qro + 64 * st + 32 * hh + 16);
     }
   }
 
@@ -172,9 +179,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   if (DENSE || MASKED) {
     cnt = i + 1;
   } else {
-    cnt = ((cint_ptr)a.counts)[(int64_t)h * p.sd.total_blocks + sp.blk0 + i];
+    cnt = ((cint_ptr)a.counts)[(int64_t)h * p.sd.total_qblocks + sp.qblk0 + r];
     cnt = uniform(cnt < 0 ? 0 : (cnt > i + 1 ? i + 1 : cnt));
-    list = (cint_ptr)(a.idx + (int64_t)h * p.sd.total_tri + sp.tri0 + (int64_t)i * (i + 1) / 2);
+    // rows I0 .. i-1 of the sequence hold I0+1 .. i slots
+    list = (cint_ptr)(a.idx + (int64_t)h * p.sd.total_tri + sp.tri0 + (int64_t)r * (sp.I0 + 1) +
+                      (int64_t)r * (r - 1) / 2);
   }
   bool bad = cnt == 0;
 
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   f32x16 s0[2];
   if (MASKED) {
     typedef const __attribute__((address_space(4))) uint32_t* cu32_ptr;
-    const cu32_ptr mrow = (cu32_ptr)(a.mask + ((int64_t)h * nb + i) * a.mask_words);
+    const cu32_ptr mrow = (cu32_ptr)(a.mask + ((int64_t)h * sp.nq + r) * a.mask_words);
     unsigned word = 0;
     int visited = 0;
     for (int j = 0; j <= i; ++j) {
@@ -485,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   if (DT == 1) inv *= a.v_scale[g];
   if (bad) inv = __builtin_nanf("");
   if (qvalid) {
-    unsigned char* orow = (unsigned char*)a.out + ((sp.tok0 + tq) * a.o_st + (int64_t)h * a.o_sh) * 2;
+    unsigned char* orow = (unsigned char*)a.out + ((sp.qtok0 + tq) * a.o_st + (int64_t)h * a.o_sh) * 2;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -497,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       }
     if (LSE && hh == 0) {
       const float lse = bad ? __builtin_nanf("") : (m - SHIFT + __builtin_log2f(lsum)) * kLn2;
-      a.lse[(int64_t)h * p.sd.total_tokens + sp.tok0 + tq] = lse;
+      a.lse[(int64_t)h * p.sd.total_qtokens + sp.qtok0 + tq] = lse;
     }
   }
 }
@@ -529,7 +538,7 @@ hipError_t launch_t(const AttnK& p, dim3 grid, hipStream_t st) {
 
 hipError_t launch_attn(const AttnLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st) {
   AttnK p{a, sd, pd, a.hq / a.hkv};
-  const int64_t n_wg = (int64_t)a.hq * sd.max_nb * sd.n_seqs;
+  const int64_t n_wg = (int64_t)a.hq * sd.max_nq * sd.n_seqs;
   dim3 grid((unsigned)n_wg);
   const bool paged = pd.table != nullptr;
   if (a.mask != nullptr) {

@@ -11,14 +11,24 @@ constexpr int kBlock = 128;   // tokens per block (= page size)
 constexpr int kHeadDim = 128; // head dimension
 
 // Sequence layout of a (possibly single-sequence) batch.
+// Keys: sequence s owns key tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.  Queries:
+// in prefill the same tokens; in chunked prefill (cu_seqlens_q set) the last
+// len_q = cu_seqlens_q[s+1] - cu_seqlens_q[s] positions of the sequence, so query t
+// sits at absolute position len_k - len_q + t.  Query blocks are numbered by
+// absolute position: block I covers positions 128I .. 128I+127 (the first and
+// last can be partial); list row I holds key blocks 0..I.
 struct SeqDesc {
-  const int32_t* cu_seqlens;  // device [n_seqs+1]; nullptr: one sequence of length L
+  const int32_t* cu_seqlens;  // device [n_seqs+1] key (sequence) lengths; nullptr: one sequence of length L
+  const int32_t* cu_seqlens_q;  // device [n_seqs+1] query lengths, or nullptr: queries = keys
   int n_seqs;
   int L;                      // the single sequence's length when cu_seqlens == nullptr
-  int max_nb;                 // ceil(max_seqlen / 128): grid extent over blocks
-  int64_t total_tokens;       // declared extents of the packed buffers
+  int max_nb;                 // grid extent over key blocks
+  int max_nq;                 // grid extent over query blocks
+  int64_t total_tokens;       // declared extents of the packed key-side buffers
   int64_t total_blocks;
-  int64_t total_tri;
+  int64_t total_qtokens;      // ... and of the query-side ones (= the key side in prefill)
+  int64_t total_qblocks;
+  int64_t total_tri;          // list capacity per head
 };
 
 // Paged KV addressing (table == nullptr: packed like Q).
@@ -29,6 +39,7 @@ struct PageDesc {
 };
 
 struct PoolLaunch {
+  bool query_view;            // pool the query blocks of each sequence (else the key blocks)
   const void* x;              // [tokens, H, d] or pages [P, 128, H, d]
   const float* scale;         // fp8 per-head scale or nullptr
   int dtype;                  // 0 bf16, 1 fp8

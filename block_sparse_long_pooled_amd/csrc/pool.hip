@@ -53,15 +53,24 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolK p) {
   const int s = blockIdx.y;   // sequence
   const int hg = blockIdx.z;  // head group
   const SeqPos sp = seq_pos(p.sd, s);
-  const int nb = (sp.len + kBlock - 1) / kBlock;
-  if (i >= nb || sp.blk0 + i >= p.sd.total_blocks) return;
+  // the view: key blocks 0..nb-1 of the key tokens, or the query blocks of the
+  // query tokens (block i = absolute block I0 + i; its tokens are the positions
+  // 128(I0+i) .. 128(I0+i)+127 that the query chunk holds)
+  const bool qv = a.query_view;
+  const int nb = qv ? sp.nq : (sp.len + kBlock - 1) / kBlock;
+  const int64_t blk0 = qv ? sp.qblk0 : sp.blk0;
+  const int64_t total_blocks = qv ? p.sd.total_qblocks : p.sd.total_blocks;
+  if (i >= nb || blk0 + i >= total_blocks) return;
+  const int vlen = qv ? sp.qlen : sp.len;
+  const int voff = qv ? sp.qoff : 0;
+  const int first = max(0, (qv ? sp.I0 + i : i) * kBlock - voff);  // first token of the block in the view
+  const int n = min(vlen, (qv ? sp.I0 + i + 1 : i + 1) * kBlock - voff) - first;
 
   const int tid = threadIdx.x;
   const int chunk = tid & 15;                  // 8 consecutive elements of a head row
   const int hl = (tid >> 4) & (kHeadsPerWG - 1);
   const int r0 = tid >> 6;                     // token row lane 0..3
   const int h = hg * kHeadsPerWG + hl;
-  const int n = min(kBlock, sp.len - i * kBlock);
 
   bool bad_page = false;
   const char* base;
@@ -71,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolK p) {
     bad_page = page < 0 || page >= p.pd.num_pages;
     base = (const char*)a.x + ((int64_t)(bad_page ? 0 : page) * a.st_page) * esize;
   } else {
-    base = (const char*)a.x + ((sp.tok0 + (int64_t)i * kBlock) * a.st_tok) * esize;
+    base = (const char*)a.x + (((qv ? sp.qtok0 : sp.tok0) + first) * a.st_tok) * esize;
   }
   base += ((int64_t)h * a.st_head + chunk * 8) * esize;
   const int64_t row_step = a.st_tok * esize;
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolK p) {
     if (DT == 1) sum *= (double)a.scale[ho];
     double mean = sum / (double)n;
     if (bad_page) mean = __builtin_nan("");
-    a.out[((int64_t)ho * p.sd.total_blocks + sp.blk0 + i) * kHeadDim + (o & (kHeadDim - 1))] = mean;
+    a.out[((int64_t)ho * total_blocks + blk0 + i) * kHeadDim + (o & (kHeadDim - 1))] = mean;
   }
 }
 
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolK p) {
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st) {
   PoolK p{a, sd, pd};
   if (!a.paged) p.pd.table = nullptr;
-  dim3 grid(sd.max_nb, sd.n_seqs, (a.H + kHeadsPerWG - 1) / kHeadsPerWG);
+  dim3 grid(a.query_view ? sd.max_nq : sd.max_nb, sd.n_seqs, (a.H + kHeadsPerWG - 1) / kHeadsPerWG);
   if (a.dtype == 0)
     hipLaunchKernelGGL(pool_kernel<0>, grid, dim3(kThreads), 0, st, p);
   else

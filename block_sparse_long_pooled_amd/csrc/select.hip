@@ -29,9 +29,10 @@ struct SelK {
   SeqDesc sd;
 };
 
-// acc[4][4] = Qtile(rows tr*4..) x Ktile(cols tc*4..)^T for one (row tile, col tile).
+// acc[4][4] = Qtile(rows tr*4..) x Ktile(cols tc*4..)^T for one (row tile, col tile);
+// rows past nq and columns past nk read as zero.
 __device__ inline void tile_scores(const double* __restrict__ Qb, const double* __restrict__ Kb,
-                                   int row0, int col0, int nb, double (*Qs)[kTile], double (*Ks)[kTile],
+                                   int row0, int col0, int nq, int nk, double (*Qs)[kTile], double (*Ks)[kTile],
                                    double acc[4][4]) {
   const int tid = threadIdx.x;
   const int tr = tid >> 4, tc = tid & 15;
@@ -46,8 +47,8 @@ __device__ inline void tile_scores(const double* __restrict__ Qb, const double* 
       const int e = tid + u * kThreads;  // 0..1023 = 64 rows x 16 d
       const int rr = e >> 4, dd = e & 15;
       const int qi = row0 + rr, kj = col0 + rr;
-      Qs[dd][rr] = qi < nb ? Qb[(int64_t)qi * kHeadDim + dk0 + dd] : 0.0;
-      Ks[dd][rr] = kj < nb ? Kb[(int64_t)kj * kHeadDim + dk0 + dd] : 0.0;
+      Qs[dd][rr] = qi < nq ? Qb[(int64_t)qi * kHeadDim + dk0 + dd] : 0.0;
+      Ks[dd][rr] = kj < nk ? Kb[(int64_t)kj * kHeadDim + dk0 + dd] : 0.0;
     }
     __syncthreads();
 #pragma unroll
@@ -72,11 +73,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
   const int s = blockIdx.y;
   const int h = blockIdx.z;
   const SeqPos sp = seq_pos(p.sd, s);
-  const int nb = (sp.len + kBlock - 1) / kBlock;
+  // rows: the sequence's query blocks r = 0..nq-1, absolute block I = I0 + r;
+  // columns: its key blocks j = 0..I
+  const int nq = sp.nq;
+  const int nk = (sp.len + kBlock - 1) / kBlock;
+  const int I0 = sp.I0;
   const int row0 = it * kTile;
-  if (row0 >= nb) return;
+  if (row0 >= nq) return;
+  const int jt_last = (I0 + min(row0 + kTile, nq) - 1) / kTile;  // last key tile any row of this tile needs
   const int g = h / (a.hq / a.hkv);
-  const double* Qb = a.pq + ((int64_t)h * p.sd.total_blocks + sp.blk0) * kHeadDim;
+  const double* Qb = a.pq + ((int64_t)h * p.sd.total_qblocks + sp.qblk0) * kHeadDim;
   const double* Kb = a.pk + ((int64_t)g * p.sd.total_blocks + sp.blk0) * kHeadDim;
 
   __shared__ double Qs[kDK][kTile];
@@ -89,15 +95,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
   // pass 1: row maxima over the causal blocks j <= i
   double rmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
   double acc[4][4];
-  for (int jt = 0; jt <= it; ++jt) {
-    tile_scores(Qb, Kb, row0, jt * kTile, nb, Qs, Ks, acc);
+  for (int jt = 0; jt <= jt_last; ++jt) {
+    tile_scores(Qb, Kb, row0, jt * kTile, nq, nk, Qs, Ks, acc);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int i = row0 + tr * 4 + x;
+      const int r = row0 + tr * 4 + x;
+      const int i = I0 + r;
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int j = jt * kTile + tc * 4 + y;
-        if (j <= i && i < nb) rmax[x] = fmax(rmax[x], acc[x][y] * a.scale);
+        if (j <= i && r < nq) rmax[x] = fmax(rmax[x], acc[x][y] * a.scale);
       }
     }
   }
@@ -110,17 +117,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
   int cnt[4] = {0, 0, 0, 0};
   int32_t* idx_h = a.idx + (int64_t)h * p.sd.total_tri + sp.tri0;
   const int64_t tri_cap = p.sd.total_tri - sp.tri0;
-  for (int jt = 0; jt <= it; ++jt) {
-    tile_scores(Qb, Kb, row0, jt * kTile, nb, Qs, Ks, acc);
+  for (int jt = 0; jt <= jt_last; ++jt) {
+    tile_scores(Qb, Kb, row0, jt * kTile, nq, nk, Qs, Ks, acc);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int i = row0 + tr * 4 + x;
+      const int r = row0 + tr * 4 + x;
+      const int i = I0 + r;
       unsigned bits = 0;
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int j = jt * kTile + tc * 4 + y;
         const double sc = acc[x][y] * a.scale;
-        const bool keep = (j <= i) && (i < nb) &&
+        const bool keep = (j <= i) && (r < nq) &&
                           ((sc - rmax[x] >= a.log_alpha) || (j < a.n_sink) || (j > i - a.n_local));
         bits |= (keep ? 1u : 0u) << y;
       }
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
         word |= __shfl_xor(word, 2, 16);
         word |= __shfl_xor(word, 4, 16);
         const int wi = (jt * kTile + tc * 4) >> 5;
-        if ((tc & 7) == 0 && i < nb && wi < a.mask_words) a.mask[((int64_t)h * nb + i) * a.mask_words + wi] = word;
+        if ((tc & 7) == 0 && r < nq && wi < a.mask_words) a.mask[((int64_t)h * nq + r) * a.mask_words + wi] = word;
         continue;
       }
       const int pc = __popc(bits);
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
       }
       const int total = __shfl(incl, 15, 16);
       int pos = cnt[x] + incl - pc;
-      const int64_t rbase = (int64_t)i * (i + 1) / 2;
+      const int64_t rbase = (int64_t)r * (I0 + 1) + (int64_t)r * (r - 1) / 2;  // rows I0 .. i-1 hold I0+1 .. i slots
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         if (bits & (1u << y)) {
@@ -157,9 +165,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
   if (!MASK && tc == 0) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int i = row0 + tr * 4 + x;
-      if (i < nb && sp.blk0 + i < p.sd.total_blocks)
-        a.counts[(int64_t)h * p.sd.total_blocks + sp.blk0 + i] = cnt[x];
+      const int r = row0 + tr * 4 + x;
+      if (r < nq && sp.qblk0 + r < p.sd.total_qblocks)
+        a.counts[(int64_t)h * p.sd.total_qblocks + sp.qblk0 + r] = cnt[x];
     }
   }
 }
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
 
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st) {
   SelK p{a, sd};
-  dim3 grid((sd.max_nb + kTile - 1) / kTile, sd.n_seqs, a.hq);
+  dim3 grid((sd.max_nq + kTile - 1) / kTile, sd.n_seqs, a.hq);
   if (a.mask != nullptr) hipLaunchKernelGGL(select_kernel<true>, grid, dim3(kThreads), 0, st, p);
   else hipLaunchKernelGGL(select_kernel<false>, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();

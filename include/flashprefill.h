@@ -261,6 +261,68 @@ int fp_sparse_attn_paged(const void* q, const void* k, const void* v, int dtype,
                          const int32_t* idx, const int32_t* counts, float softmax_scale,
                          void* out, float* lse, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Chunked / prefix-cached prefill.  Each sequence brings len_q new query tokens
+ * against a K/V cache of len_k >= len_q tokens that already holds them (the
+ * prefix plus this chunk): query t of the sequence sits at absolute position
+ * len_k - len_q + t and attends causally to keys 0 .. that position (the
+ * causal mask is aligned to the bottom-right corner).  With len_q = len_k this is
+ * the prefill above.
+ *
+ *   cu_seqlens_q  device int32 [n_seqs + 1]: query lengths, packed Q / out / LSE
+ *   cu_seqlens_k  device int32 [n_seqs + 1]: key lengths, packed K/V when
+ *                 page_table is NULL (else K/V pages as in the paged calls)
+ *   max_seqlen_q/k  host bounds on the lengths (size the launch grids)
+ *   total_q/total_k packed token extents
+ *   Query blocks follow absolute positions: block I holds positions
+ *   128I .. 128I+127, so a chunk that starts inside a block has a partial first
+ *   query block.  Sequence s has nq_s query blocks I0_s .. I0_s+nq_s-1 (I0_s =
+ *   (len_k - len_q) / 128) and nk_s = ceil(len_k / 128) key blocks.
+ *   pooled_q   [hq, total_qblocks, d], total_qblocks = sum_s nq_s, sequences in
+ *              order; a query block is the mean of the chunk's tokens in it
+ *   pooled_k   [hkv, total_kblocks, d], total_kblocks = sum_s nk_s
+ *   idx        list row of (h, s, I) at h*total_tri + tri_s + (I-I0_s)(I0_s+1)
+ *              + (I-I0_s)(I-I0_s-1)/2 with tri_s = sum over earlier sequences of
+ *              nq(I0+1) + nq(nq-1)/2 (row I has I+1 slots); total_tri = that sum
+ *              over all sequences
+ *   counts     [hq, total_qblocks] int32
+ *   out, lse   [total_q, hq, d] bf16, [hq, total_q] fp32
+ * Selection rules, dtypes and error behaviour as in the calls above; query
+ * lengths above the key length are clamped to it.
+ * ------------------------------------------------------------------------- */
+int fp_discover_chunked(const void* q, const void* k, int dtype,
+                        const float* q_scale, const float* k_scale,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seqs,
+                        int max_seqlen_q, int max_seqlen_k, int64_t total_q, int64_t total_k,
+                        int64_t total_qblocks, int64_t total_kblocks,
+                        const int32_t* page_table, int max_pages, int num_pages,
+                        int hq, int hkv, int d, int block,
+                        int64_t q_stride_tok, int64_t q_stride_head,
+                        int64_t k_stride_page, int64_t k_stride_tok, int64_t k_stride_head,
+                        double* pooled_q, double* pooled_k, void* stream);
+
+int fp_threshold_compact_chunked(const double* pooled_q, const double* pooled_k,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seqs,
+                                 int max_seqlen_q, int max_seqlen_k,
+                                 int64_t total_qblocks, int64_t total_kblocks, int64_t total_tri,
+                                 int hq, int hkv, int d,
+                                 double softmax_scale, double alpha, int n_sink, int n_local,
+                                 int32_t* idx, int32_t* counts, void* stream);
+
+int fp_sparse_attn_chunked(const void* q, const void* k, const void* v, int dtype,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seqs,
+                           int max_seqlen_q, int max_seqlen_k, int64_t total_q, int64_t total_k,
+                           int64_t total_qblocks, int64_t total_kblocks, int64_t total_tri,
+                           const int32_t* page_table, int max_pages, int num_pages,
+                           int hq, int hkv, int d, int block,
+                           int64_t q_stride_tok, int64_t q_stride_head,
+                           int64_t k_stride_page, int64_t k_stride_tok, int64_t k_stride_head,
+                           int64_t v_stride_page, int64_t v_stride_tok, int64_t v_stride_head,
+                           int64_t o_stride_tok, int64_t o_stride_head,
+                           const int32_t* idx, const int32_t* counts, float softmax_scale,
+                           void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

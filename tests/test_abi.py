@@ -157,6 +157,28 @@ def test_paged_rejects():
     assert rc == EINVAL
 
 
+def test_chunked_rejects():
+    lib = _lib.load()
+    # no query lengths
+    rc = lib.fp_threshold_compact_chunked(P, P, None, P, 2, 300, 1000, 12, 16, 200, 4, 2, 128, 0.088, 0.1, 1, 1,
+                                          P, P, None)
+    assert rc == EINVAL and b"cu_seqlens_q" in lib.fp_last_error()
+    # negative query extent
+    rc = lib.fp_discover_chunked(P, P, 0, None, None, P, P, 2, 300, 1000, -1, 1500, 12, 16, None, 0, 0, 4, 2, 128,
+                                 128, 512, 128, 0, 256, 128, P, P, None)
+    assert rc == EINVAL
+    # page table narrower than the key blocks
+    rc = lib.fp_sparse_attn_chunked(P, P, P, 0, None, None, None, P, P, 2, 300, 1000, 400, 1500, 12, 16, 200,
+                                    P, 3, 20, 4, 2, 128, 128, 512, 128, 32768, 256, 128, 32768, 256, 128, 512, 128,
+                                    P, P, 0.088, P, None, None)
+    assert rc == EINVAL and b"max_pages" in lib.fp_last_error()
+    # bad head dimension
+    rc = lib.fp_sparse_attn_chunked(P, P, P, 0, None, None, None, P, P, 2, 300, 1000, 400, 1500, 12, 16, 200,
+                                    None, 0, 0, 4, 2, 64, 128, 512, 128, 0, 256, 128, 0, 256, 128, 512, 128,
+                                    P, P, 0.088, P, None, None)
+    assert rc == EUNSUP
+
+
 def test_empty_inputs_are_a_no_op():
     """L = 0 validates and returns FP_OK without launching anything."""
     assert discover(L=0) == _lib.FP_OK
