@@ -127,6 +127,49 @@ def time_hot_path(wl, steps, warmup, alpha):
     return res
 
 
+def time_chunked(r, wl, alpha, chunk, reps=3):
+    """Prefix-cached prefill on the same inputs: the last `chunk` queries against the
+    whole K/V cache (discover + threshold + attention, HIP events per stage)."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    q, k, v, qs, ks, vs, _ = r["tensors"]
+    L = q.shape[0]
+    qc = q[L - chunk:]
+    batch = fp.ChunkedBatch([chunk], [L], q.device)
+    out = torch.empty((chunk, q.shape[1], q.shape[2]), dtype=torch.bfloat16, device=q.device)
+
+    def once(ev=None):
+        if ev:
+            ev[0].record()
+        pq, pk = fp.discover_chunked(qc, k, batch, q_scale=qs, k_scale=ks)
+        if ev:
+            ev[1].record()
+        idx, counts = fp.threshold_compact_chunked(pq, pk, batch, alpha, wl.n_sink, wl.n_local)
+        if ev:
+            ev[2].record()
+        fp.sparse_attn_chunked(qc, k, v, batch, idx, counts, q_scale=qs, k_scale=ks, v_scale=vs, out=out)
+        if ev:
+            ev[3].record()
+        return counts
+
+    counts = once()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for e in evs:
+        once(e)
+    torch.cuda.synchronize()
+    st = np.array([[e[x].elapsed_time(e[x + 1]) for x in range(3)] for e in evs]).mean(axis=0)
+    tiles = int(counts.sum().item())
+    return {
+        "workload": f"{wl.name}: last {chunk} queries against the {L}-token cache",
+        "stage_ms": {"discover": float(st[0]), "threshold_compact": float(st[1]), "sparse_attn": float(st[2])},
+        "ms": float(st.sum()),
+        "listed_tiles": tiles,
+        "attn_computed_tflops": tiles * 4.0 * BLOCK * BLOCK * q.shape[2] / (st[2] * 1e-3) / 1e12,
+    }
+
+
 def time_logical_skip(r, wl, alpha, reps=2):
     """The same selection as a bit-packed mask and the masked loop over every causal
     block (the logical skipping that list compaction replaces)."""
@@ -268,6 +311,9 @@ def main():
             "note": "masked loop over every causal block, same selection; outputs bit-identical",
         }
         log(f"logical-skip attention {am:.2f} ms (lists: {r['attn_ms']:.2f} ms)")
+    if not args.no_ablation and wl.L >= 8 * 16384:
+        extra["chunked_prefill"] = time_chunked(r, wl, alpha, 16384)
+        log(f"chunked prefill (16K of {wl.L}) {extra['chunked_prefill']['ms']:.2f} ms")
     del r["tensors"], r["pooled"]
 
     if not args.no_extra and args.config == 2:
