@@ -5,11 +5,12 @@
 // the kept block ids of every row into a contiguous ascending list).
 //
 // One workgroup owns a tile of 64 query blocks of one (sequence, query head)
-// and sweeps the causal key-block tiles 0..(its own) twice: pass 1 computes
-// the fp64 scores and the row maxima, pass 2 recomputes them, tests
-// s - max >= ln(alpha) (or sink / local), and compacts.  Scores are fp64 dot
-// products of the fp64 pooled means, tiled 64x64 with a 16-wide d-chunk in
-// LDS; each thread owns a 4x4 sub-tile.  Compaction: the 16 lanes that share
+// and sweeps the key-block tiles its rows need twice: pass 1 computes the fp64
+// scores and the row maxima, pass 2 recomputes them, tests s - max >= ln(alpha)
+// (or sink / local), and compacts.  Scores are fp64 dot products of the fp64
+// pooled means in 64x64 tiles: the query tile stays in LDS for both passes, key
+// tiles stream through LDS with the next one already in registers, and each
+// thread owns a 4x4 sub-tile.  Row tiles with the longest rows start first.  Compaction: the 16 lanes that share
 // a row hold 4 consecutive columns each, so a 16-lane exclusive prefix sum of
 // the per-lane keep counts gives every kept id its slot, ascending by
 // construction.  The logical-skip ablation asks for the same decisions as a
@@ -21,7 +22,6 @@ namespace fp {
 namespace {
 
 constexpr int kTile = 64;
-constexpr int kDK = 16;
 constexpr int kThreads = 256;
 
 struct SelK {
@@ -29,96 +29,110 @@ struct SelK {
   SeqDesc sd;
 };
 
-// acc[4][4] = Qtile(rows tr*4..) x Ktile(cols tc*4..)^T for one (row tile, col tile);
-// rows past nq and columns past nk read as zero.
-__device__ inline void tile_scores(const double* __restrict__ Qb, const double* __restrict__ Kb,
-                                   int row0, int col0, int nq, int nk, double (*Qs)[kTile], double (*Ks)[kTile],
-                                   double acc[4][4]) {
-  const int tid = threadIdx.x;
-  const int tr = tid >> 4, tc = tid & 15;
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-  for (int dk0 = 0; dk0 < kHeadDim; dk0 += kDK) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = tid + u * kThreads;  // 0..1023 = 64 rows x 16 d
-      const int rr = e >> 4, dd = e & 15;
-      const int qi = row0 + rr, kj = col0 + rr;
-      Qs[dd][rr] = qi < nq ? Qb[(int64_t)qi * kHeadDim + dk0 + dd] : 0.0;
-      Ks[dd][rr] = kj < nk ? Kb[(int64_t)kj * kHeadDim + dk0 + dd] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int dd = 0; dd < kDK; ++dd) {
-      double qv[4], kv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) qv[x] = Qs[dd][tr * 4 + x];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) kv[y] = Ks[dd][tc * 4 + y];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(qv[x], kv[y], acc[x][y]);
-    }
-  }
-}
-
 template <bool MASK>
-__global__ __launch_bounds__(kThreads) void select_kernel(SelK p) {
+__global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
   const SelectLaunch& a = p.a;
-  const int it = blockIdx.x;
+  const int it = gridDim.x - 1 - blockIdx.x;  // row tiles with the longest rows first
   const int s = blockIdx.y;
   const int h = blockIdx.z;
   const SeqPos sp = seq_pos(p.sd, s);
   // rows: the sequence's query blocks r = 0..nq-1, absolute block I = I0 + r;
   // columns: its key blocks j = 0..I
-  const int nq = sp.nq;
-  const int nk = (sp.len + kBlock - 1) / kBlock;
+  // (clamped to the declared extents so inconsistent metadata cannot read past them)
+  const int nq = (int)min((int64_t)sp.nq, max((int64_t)0, p.sd.total_qblocks - sp.qblk0));
+  const int nk = (int)min((int64_t)(sp.len + kBlock - 1) / kBlock, max((int64_t)0, p.sd.total_blocks - sp.blk0));
   const int I0 = sp.I0;
   const int row0 = it * kTile;
   if (row0 >= nq) return;
-  const int jt_last = (I0 + min(row0 + kTile, nq) - 1) / kTile;  // last key tile any row of this tile needs
+  const int nt = (I0 + min(row0 + kTile, nq) - 1) / kTile + 1;  // key tiles any row of this tile needs
   const int g = h / (a.hq / a.hkv);
   const double* Qb = a.pq + ((int64_t)h * p.sd.total_qblocks + sp.qblk0) * kHeadDim;
   const double* Kb = a.pk + ((int64_t)g * p.sd.total_blocks + sp.blk0) * kHeadDim;
 
-  __shared__ double Qs[kDK][kTile];
-  __shared__ double Ks[kDK][kTile];
+  // The query tile stays in LDS for both passes; key tiles stream through LDS and
+  // the next one is in registers while the current one is used.  d-major layout:
+  // a thread reads 4 consecutive rows (or columns) of one d as two 16-byte reads.
+  __shared__ __attribute__((aligned(16))) double Qs[kHeadDim][kTile];
+  __shared__ __attribute__((aligned(16))) double Ks[kHeadDim][kTile];
 
   const int tid = threadIdx.x;
   const int tr = tid >> 4, tc = tid & 15;
   const double NEG_INF = -__builtin_huge_val();
 
-  // pass 1: row maxima over the causal blocks j <= i
-  double rmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-  double acc[4][4];
-  for (int jt = 0; jt <= jt_last; ++jt) {
-    tile_scores(Qb, Kb, row0, jt * kTile, nq, nk, Qs, Ks, acc);
+  // staging: thread t moves row t/4, d = 32(t%4) .. +31 of a 64-row tile
+  typedef __attribute__((ext_vector_type(2))) double f64x2;
+  f64x2 reg[16];
+  auto load_rows = [&](const double* base, int first, int nrows) {
+    const int rr = tid >> 2, d0 = (tid & 3) * 32;
+    const bool ok = first + rr < nrows;
+    const f64x2* src = (const f64x2*)(base + (int64_t)(first + rr) * kHeadDim + d0);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int r = row0 + tr * 4 + x;
-      const int i = I0 + r;
+    for (int u = 0; u < 16; ++u) reg[u] = ok ? src[u] : f64x2{0.0, 0.0};
+  };
+  auto store_rows = [&](double (*S)[kTile]) {
+    const int rr = tid >> 2, d0 = (tid & 3) * 32;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = jt * kTile + tc * 4 + y;
-        if (j <= i && r < nq) rmax[x] = fmax(rmax[x], acc[x][y] * a.scale);
-      }
+    for (int u = 0; u < 16; ++u) {
+      S[d0 + 2 * u][rr] = reg[u][0];
+      S[d0 + 2 * u + 1][rr] = reg[u][1];
     }
-  }
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) rmax[x] = fmax(rmax[x], __shfl_xor(rmax[x], off, 16));
+  };
 
-  // pass 2: threshold + compaction
+  double acc[4][4];
+  auto tile_scores = [&]() {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+#pragma unroll 8
+    for (int dd = 0; dd < kHeadDim; ++dd) {
+      const f64x2 q01 = *(const f64x2*)&Qs[dd][tr * 4], q23 = *(const f64x2*)&Qs[dd][tr * 4 + 2];
+      const f64x2 k01 = *(const f64x2*)&Ks[dd][tc * 4], k23 = *(const f64x2*)&Ks[dd][tc * 4 + 2];
+      const double qv[4] = {q01[0], q01[1], q23[0], q23[1]};
+      const double kv[4] = {k01[0], k01[1], k23[0], k23[1]};
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(qv[x], kv[y], acc[x][y]);
+    }
+  };
+
+  load_rows(Qb, row0, nq);
+  store_rows(Qs);
+  load_rows(Kb, 0, nk);
+
+  double rmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
   int cnt[4] = {0, 0, 0, 0};
   int32_t* idx_h = a.idx + (int64_t)h * p.sd.total_tri + sp.tri0;
   const int64_t tri_cap = p.sd.total_tri - sp.tri0;
-  for (int jt = 0; jt <= jt_last; ++jt) {
-    tile_scores(Qb, Kb, row0, jt * kTile, nq, nk, Qs, Ks, acc);
+  // pass 1 (q < nt): row maxima over the causal blocks j <= I; pass 2: threshold +
+  // compaction, recomputing the same scores
+  for (int q = 0; q < 2 * nt; ++q) {
+    const int jt = q < nt ? q : q - nt;
+    __syncthreads();  // every thread is done with the previous key tile
+    store_rows(Ks);
+    __syncthreads();
+    if (q + 1 < 2 * nt) load_rows(Kb, ((q + 1) % nt) * kTile, nk);
+    tile_scores();
+    if (q < nt) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = row0 + tr * 4 + x;
+        const int i = I0 + r;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int j = jt * kTile + tc * 4 + y;
+          if (j <= i && r < nq) rmax[x] = fmax(rmax[x], acc[x][y] * a.scale);
+        }
+      }
+      if (q == nt - 1) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rmax[x] = fmax(rmax[x], __shfl_xor(rmax[x], off, 16));
+      }
+      continue;
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int r = row0 + tr * 4 + x;
