@@ -8,14 +8,14 @@
 // and sweeps the key-block tiles its rows need twice: pass 1 computes the fp64
 // scores and the row maxima, pass 2 recomputes them, tests s - max >= ln(alpha)
 // (or sink / local), and compacts.  Scores are fp64 dot products of the fp64
-// pooled means in 64x64 tiles: the query tile stays in LDS for both passes, key
-// tiles stream through LDS with the next one already in registers, and each
-// thread owns a 4x4 sub-tile.  Row tiles with the longest rows start first.  Compaction: the 16 lanes that share
-// a row hold 4 consecutive columns each, so a 16-lane exclusive prefix sum of
-// the per-lane keep counts gives every kept id its slot, ascending by
-// construction.  The logical-skip ablation asks for the same decisions as a
-// bit-packed block mask instead of lists (32 blocks per word, bit j%32 of word
-// j/32 of row i).
+// pooled means in 64x64 tiles on the fp64 matrix core: the query tile stays in
+// LDS for both passes and key tiles stream through LDS with the next one
+// already in registers.  Row tiles with the longest rows start first.
+// Compaction: the 16 lanes that share a row hold one column of each 16-column
+// slice, so a ballot per slice and a popcount of the lower lanes give every
+// kept id its slot, ascending by construction.  The logical-skip ablation asks
+// for the same decisions as a bit-packed block mask instead of lists (32 blocks
+// per word, bit j%32 of word j/32 of row i).
 #include "fp_device.h"
 
 namespace fp {
@@ -56,11 +56,15 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
   __shared__ __attribute__((aligned(16))) double Ks[kHeadDim][kTile];
 
   const int tid = threadIdx.x;
-  const int tr = tid >> 4, tc = tid & 15;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int lg = lane >> 4;   // 16-lane group
+  const int lc = lane & 15;   // lane within the group
   const double NEG_INF = -__builtin_huge_val();
 
   // staging: thread t moves row t/4, d = 32(t%4) .. +31 of a 64-row tile
   typedef __attribute__((ext_vector_type(2))) double f64x2;
+  typedef __attribute__((ext_vector_type(4))) double f64x4;
   f64x2 reg[16];
   auto load_rows = [&](const double* base, int first, int nrows) {
     const int rr = tid >> 2, d0 = (tid & 3) * 32;
@@ -78,22 +82,22 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
     }
   };
 
-  double acc[4][4];
+  // Scores on the fp64 matrix core (v_mfma_f64_16x16x4_f64: A lane = row l%16 at
+  // k = l/16, B lane = column l%16 at k = l/16, C element v of lane l = row
+  // l/16 + 4v, column l%16).  Wave w owns tile rows 16w .. 16w+15 and all 64
+  // columns as four 16x16 products, so a row's 64 scores live in one 16-lane
+  // group: lane lc of group lg holds rows 16w + lg + 4v (v = 0..3) at columns
+  // 16t + lc (t = 0..3) in acc[t][v].
+  f64x4 acc[4];
   auto tile_scores = [&]() {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+    for (int t = 0; t < 4; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
-    for (int dd = 0; dd < kHeadDim; ++dd) {
-      const f64x2 q01 = *(const f64x2*)&Qs[dd][tr * 4], q23 = *(const f64x2*)&Qs[dd][tr * 4 + 2];
-      const f64x2 k01 = *(const f64x2*)&Ks[dd][tc * 4], k23 = *(const f64x2*)&Ks[dd][tc * 4 + 2];
-      const double qv[4] = {q01[0], q01[1], q23[0], q23[1]};
-      const double kv[4] = {k01[0], k01[1], k23[0], k23[1]};
+    for (int ks = 0; ks < kHeadDim / 4; ++ks) {
+      const double av = Qs[4 * ks + lg][16 * w + lc];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(qv[x], kv[y], acc[x][y]);
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Ks[4 * ks + lg][16 * t + lc], acc[t], 0, 0, 0);
     }
   };
 
@@ -116,72 +120,62 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
     tile_scores();
     if (q < nt) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int r = row0 + tr * 4 + x;
+      for (int v = 0; v < 4; ++v) {
+        const int r = row0 + 16 * w + lg + 4 * v;
         const int i = I0 + r;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int j = jt * kTile + tc * 4 + y;
-          if (j <= i && r < nq) rmax[x] = fmax(rmax[x], acc[x][y] * a.scale);
+        for (int t = 0; t < 4; ++t) {
+          const int j = jt * kTile + 16 * t + lc;
+          if (j <= i && r < nq) rmax[v] = fmax(rmax[v], acc[t][v] * a.scale);
         }
       }
       if (q == nt - 1) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rmax[x] = fmax(rmax[x], __shfl_xor(rmax[x], off, 16));
+          for (int off = 1; off < 16; off <<= 1) rmax[v] = fmax(rmax[v], __shfl_xor(rmax[v], off, 16));
       }
       continue;
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int r = row0 + tr * 4 + x;
+    for (int v = 0; v < 4; ++v) {
+      const int r = row0 + 16 * w + lg + 4 * v;
       const int i = I0 + r;
-      unsigned bits = 0;
+      const int64_t rbase = (int64_t)r * (I0 + 1) + (int64_t)r * (r - 1) / 2;  // rows I0 .. i-1 hold I0+1 .. i slots
+      unsigned gb[4];  // keep bits of the 16 columns 16t .. 16t+15 of this lane's row
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int j = jt * kTile + tc * 4 + y;
-        const double sc = acc[x][y] * a.scale;
+      for (int t = 0; t < 4; ++t) {
+        const int j = jt * kTile + 16 * t + lc;
+        const double sc = acc[t][v] * a.scale;
         const bool keep = (j <= i) && (r < nq) &&
-                          ((sc - rmax[x] >= a.log_alpha) || (j < a.n_sink) || (j > i - a.n_local));
-        bits |= (keep ? 1u : 0u) << y;
+                          ((sc - rmax[v] >= a.log_alpha) || (j < a.n_sink) || (j > i - a.n_local));
+        gb[t] = (unsigned)(__ballot(keep) >> (16 * lg)) & 0xffffu;
       }
       if (MASK) {
-        // the 8 lanes tc&~7 .. tc|7 hold the 32 columns of one word of row i
-        unsigned word = bits << (4 * (tc & 7));
-        word |= __shfl_xor(word, 1, 16);
-        word |= __shfl_xor(word, 2, 16);
-        word |= __shfl_xor(word, 4, 16);
-        const int wi = (jt * kTile + tc * 4) >> 5;
-        if ((tc & 7) == 0 && r < nq && wi < a.mask_words) a.mask[((int64_t)h * nq + r) * a.mask_words + wi] = word;
+        // words 2jt and 2jt+1 of the row: columns 0..31 and 32..63 of this tile
+        if (lc < 2 && r < nq) {
+          const int wi = 2 * jt + lc;
+          if (wi < a.mask_words)
+            a.mask[((int64_t)h * nq + r) * a.mask_words + wi] = gb[2 * lc] | (gb[2 * lc + 1] << 16);
+        }
         continue;
       }
-      const int pc = __popc(bits);
-      int incl = pc;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const int v = __shfl_up(incl, off, 16);
-        if (tc >= off) incl += v;
-      }
-      const int total = __shfl(incl, 15, 16);
-      int pos = cnt[x] + incl - pc;
-      const int64_t rbase = (int64_t)r * (I0 + 1) + (int64_t)r * (r - 1) / 2;  // rows I0 .. i-1 hold I0+1 .. i slots
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        if (bits & (1u << y)) {
-          if (rbase + pos < tri_cap) idx_h[rbase + pos] = jt * kTile + tc * 4 + y;
-          ++pos;
+      for (int t = 0; t < 4; ++t) {
+        if (gb[t] & (1u << lc)) {
+          const int64_t pos = cnt[v] + __popc(gb[t] & ((1u << lc) - 1u));
+          if (rbase + pos < tri_cap) idx_h[rbase + pos] = jt * kTile + 16 * t + lc;
         }
+        cnt[v] += __popc(gb[t]);
       }
-      cnt[x] += total;
     }
   }
-  if (!MASK && tc == 0) {
+  if (!MASK && lc == 0) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int r = row0 + tr * 4 + x;
+    for (int v = 0; v < 4; ++v) {
+      const int r = row0 + 16 * w + lg + 4 * v;
       if (r < nq && sp.qblk0 + r < p.sd.total_qblocks)
-        a.counts[(int64_t)h * p.sd.total_qblocks + sp.qblk0 + r] = cnt[x];
+        a.counts[(int64_t)h * p.sd.total_qblocks + sp.qblk0 + r] = cnt[v];
     }
   }
 }
