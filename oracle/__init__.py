@@ -37,6 +37,9 @@ it is used):
 * varlen/paged: every sequence is processed on its own with queries and keys
   starting at token 0; the page table is addressing only, so it never appears
   here;
+* group-shared lists (a PackGQA-style mode, beyond what the pages define): the
+  list of a KV-head group is the union of its query heads' lists, and every
+  query head of the group attends over that union (a superset of its own list);
 * chunked / prefix-cached prefill (beyond the pages, which only name paged KV
   and continuous batching for serving): a chunk of len_q queries is the last
   len_q positions of a sequence whose K/V cache holds len_k tokens; query t sits
@@ -67,6 +70,7 @@ __all__ = [
     "keep_mask", "compact", "select_blocks", "attend_block", "sparse_attention",
     "dense_attention", "select_blocks_varlen", "sparse_attention_varlen", "dense_attention_varlen",
     "chunk_blocks", "pool_chunk", "select_blocks_chunked", "sparse_attention_chunked",
+    "select_blocks_grouped",
 ]
 
 
@@ -359,3 +363,21 @@ def sparse_attention_chunked(qc: np.ndarray, k: np.ndarray, v: np.ndarray, lists
             out[t, h, :] = (e @ v[c, g, :]) / e.sum()
             lse[h, t] = M + np.log(e.sum())
     return (out, lse) if want_lse else out
+
+
+# ------------------------------------------------------- group-shared lists
+def select_blocks_grouped(q: np.ndarray, k: np.ndarray, block: int, alpha: float, n_sink: int,
+                          n_local: int, scale: Optional[float] = None) -> Dict[str, object]:
+    """Per-head selection as in ``select_blocks``, then one list per KV-head group:
+    the union of the keep masks of the group's query heads.  Returns the per-head
+    result under ``heads`` plus the group keep mask, lists and counts."""
+    per_head = select_blocks(q, k, block, alpha, n_sink, n_local, scale)
+    keep = per_head["keep"]
+    hq = keep.shape[0]
+    hkv = k.shape[1]
+    group = hq // hkv
+    gkeep = np.zeros((hkv,) + keep.shape[1:], dtype=bool)
+    for h in range(hq):
+        gkeep[h // group] |= keep[h]
+    lists, counts = compact(gkeep)
+    return dict(heads=per_head, keep=gkeep, lists=lists, counts=counts)

@@ -422,3 +422,42 @@ def test_chunked_selection_brute_force():
                     if math.exp(scores[j] - m) >= alpha or j < n_sink or j > I - n_local]
             assert list(sel["lists"][h][r]) == want
             assert I < nk
+
+
+
+# ------------------------------------------------------- group-shared lists
+def test_grouped_lists_are_unions_brute_force():
+    """Group list = set union of the group's per-head lists (pure Python), ascending,
+    a superset of each head's list, ending with the diagonal."""
+    L, block = 6 * 16 + 3, 16
+    q, k = rand(L, 6, 8), rand(L, 2, 8)
+    sel = O.select_blocks_grouped(q, k, block, 0.2, 1, 2)
+    heads = sel["heads"]["lists"]
+    for g in range(2):
+        for i in range(len(sel["lists"][g])):
+            want = sorted(set().union(*[set(int(x) for x in heads[h][i]) for h in range(3 * g, 3 * g + 3)]))
+            assert [int(x) for x in sel["lists"][g][i]] == want
+            assert want[-1] == i
+
+
+def test_grouped_with_one_head_per_group_is_per_head():
+    L, block = 5 * 16, 16
+    q, k = rand(L, 3, 8), rand(L, 3, 8)
+    a = O.select_blocks_grouped(q, k, block, 0.1, 1, 1)
+    b = O.select_blocks(q, k, block, 0.1, 1, 1)
+    assert np.array_equal(a["keep"], b["keep"])
+
+
+def test_grouped_alpha_zero_and_above_one():
+    """alpha = 0 keeps every causal block for the group; alpha > 1 keeps exactly the
+    forced blocks (closed forms, as for per-head lists)."""
+    L, block = 5 * 16 + 9, 16
+    q, k = rand(L, 4, 8), rand(L, 2, 8)
+    nb = -(-L // block)
+    full = O.select_blocks_grouped(q, k, block, 0.0, 1, 1)
+    assert np.array_equal(full["keep"], np.broadcast_to(np.tril(np.ones((nb, nb), dtype=bool)), (2, nb, nb)))
+    forced = O.select_blocks_grouped(q, k, block, 1.5, 2, 2)
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    want = (j <= i) & ((j < 2) | (j > i - 2))
+    assert np.array_equal(forced["keep"], np.broadcast_to(want, (2, nb, nb)))
