@@ -125,7 +125,7 @@ def _attn(name, q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, 
     args = [_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
             L, hq, hkv, d, BLOCK, q.stride(0), q.stride(1), k.stride(0), k.stride(1),
             v.stride(0), v.stride(1), out.stride(0), out.stride(1)]
-    if name == "fp_sparse_attn":
+    if name in ("fp_sparse_attn", "fp_sparse_attn_grouped"):
         args += [_ptr(idx), _ptr(counts)]
     elif name == "fp_sparse_attn_masked":
         args += [_ptr(idx)]
@@ -138,6 +138,27 @@ def sparse_attn(q, k, v, idx, counts, q_scale=None, k_scale=None, v_scale=None, 
                 out=None, return_lse=False):
     """Causal GQA attention of Q [L, hq, 128] over the listed K/V blocks -> bf16 [L, hq, 128]."""
     return _attn("fp_sparse_attn", q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out, return_lse)
+
+
+def union_compact(mask, hkv: int, idx=None, counts=None):
+    """Group-shared lists: the union of the per-head masks (from threshold_mask) of
+    every KV group, as ascending lists -> (idx [hkv * nb(nb+1)/2] int32,
+    counts [hkv, nb] int32)."""
+    hq, nb, _ = mask.shape
+    if idx is None:
+        idx = torch.zeros(idx_capacity(hkv, nb), dtype=torch.int32, device=mask.device)
+    if counts is None:
+        counts = torch.empty((hkv, nb), dtype=torch.int32, device=mask.device)
+    call("fp_union_compact", _ptr(mask), nb, hq, hkv, _ptr(idx), _ptr(counts), _stream(mask))
+    return idx, counts
+
+
+def sparse_attn_grouped(q, k, v, idx, counts, q_scale=None, k_scale=None, v_scale=None, softmax_scale=None,
+                        out=None, return_lse=False):
+    """sparse_attn with one list per KV group (from union_compact): every query head
+    attends over its group's list."""
+    return _attn("fp_sparse_attn_grouped", q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out,
+                 return_lse)
 
 
 def sparse_attn_masked(q, k, v, mask, q_scale=None, k_scale=None, v_scale=None, softmax_scale=None,

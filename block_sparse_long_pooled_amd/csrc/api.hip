@@ -280,7 +280,7 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
                        int hq, int hkv, int64_t q_st, int64_t q_sh, int64_t k_sp, int64_t k_st, int64_t k_sh,
                        int64_t v_sp, int64_t v_st, int64_t v_sh, int64_t o_st, int64_t o_sh,
                        const int32_t* idx, const int32_t* counts, float softmax_scale, void* out, float* lse,
-                       void* stream, const uint32_t* mask = nullptr) {
+                       void* stream, const uint32_t* mask = nullptr, int list_div = 1) {
   int r;
   if ((r = check_tensor("q", q, dtype, q_st, q_sh))) return r;
   if ((r = check_tensor("k", k, dtype, k_st, k_sh))) return r;
@@ -306,7 +306,37 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
   a.v_sp = v_sp; a.v_st = v_st; a.v_sh = v_sh; a.o_st = o_st; a.o_sh = o_sh;
   a.idx = idx; a.counts = counts; a.softmax_scale = softmax_scale; a.out = out; a.lse = lse;
   a.mask = mask; a.mask_words = (int)((sd.max_nb + 31) / 32);
+  a.list_div = list_div;
   return launch_status(fp::launch_attn(a, sd, pd, (hipStream_t)stream));
+}
+
+int fp_union_compact(const uint32_t* mask, int nb, int hq, int hkv, int32_t* idx, int32_t* counts, void* stream) {
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return fail(FP_EINVAL, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
+  if (nb < 0 || nb > (1 << 24)) return fail(FP_EINVAL, "nb=%d out of range", nb);
+  if (nb == 0) return ok();
+  if (mask == nullptr || idx == nullptr || counts == nullptr) return fail(FP_EINVAL, "mask/idx/counts is NULL");
+  if ((uintptr_t)mask & 3u) return fail(FP_EINVAL, "mask not 4-byte aligned");
+  fp::UnionLaunch a{mask, hq, hkv, nb, (int)((nb + 31) / 32), idx, counts};
+  return launch_status(fp::launch_union(a, (hipStream_t)stream));
+}
+
+int fp_sparse_attn_grouped(const void* q, const void* k, const void* v, int dtype,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           int L, int hq, int hkv, int d, int block,
+                           int64_t q_stride_tok, int64_t q_stride_head, int64_t k_stride_tok, int64_t k_stride_head,
+                           int64_t v_stride_tok, int64_t v_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                           const int32_t* idx, const int32_t* counts, float softmax_scale,
+                           void* out, float* lse, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
+  if (L < 0) return fail(FP_EINVAL, "L < 0");
+  if (L == 0) return ok();
+  if (idx == nullptr || counts == nullptr) return fail(FP_EINVAL, "idx/counts is NULL");
+  if ((int64_t)hq * nblocks(L) >= (int64_t)1 << 31) return fail(FP_EINVAL, "grid too large");
+  fp::PageDesc pd{nullptr, 0, 0};
+  return attn_common(q, k, v, dtype, q_scale, k_scale, v_scale, single_seq(L), pd, hq, hkv,
+                     q_stride_tok, q_stride_head, 0, k_stride_tok, k_stride_head, 0, v_stride_tok, v_stride_head,
+                     o_stride_tok, o_stride_head, idx, counts, softmax_scale, out, lse, stream, nullptr, hq / hkv);
 }
 
 int fp_sparse_attn_masked(const void* q, const void* k, const void* v, int dtype,

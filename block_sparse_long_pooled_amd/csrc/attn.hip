@@ -179,10 +179,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   if (DENSE || MASKED) {
     cnt = i + 1;
   } else {
-    cnt = ((cint_ptr)a.counts)[(int64_t)h * p.sd.total_qblocks + sp.qblk0 + r];
+    const int hl = h / a.list_div;  // the list this head reads (per head, or per KV group)
+    cnt = ((cint_ptr)a.counts)[(int64_t)hl * p.sd.total_qblocks + sp.qblk0 + r];
     cnt = uniform(cnt < 0 ? 0 : (cnt > i + 1 ? i + 1 : cnt));
     // rows I0 .. i-1 of the sequence hold I0+1 .. i slots
-    list = (cint_ptr)(a.idx + (int64_t)h * p.sd.total_tri + sp.tri0 + (int64_t)r * (sp.I0 + 1) +
+    list = (cint_ptr)(a.idx + (int64_t)hl * p.sd.total_tri + sp.tri0 + (int64_t)r * (sp.I0 + 1) +
                       (int64_t)r * (r - 1) / 2);
   }
   bool bad = cnt == 0;

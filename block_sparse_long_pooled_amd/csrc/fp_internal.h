@@ -78,7 +78,18 @@ struct AttnLaunch {
   float* lse;                 // [hq, total_tokens] or nullptr
   const uint32_t* mask;       // logical-skip mode: bit-packed keep mask [hq, nb, mask_words], or nullptr
   int mask_words;
+  int list_div;               // query head h reads list h / list_div (1: per head; hq/hkv: per KV group)
 };
+
+// Union of the per-head block masks of every KV group, compacted to ascending
+// lists (group-shared lists).
+struct UnionLaunch {
+  const uint32_t* mask;       // [hq, nb, mask_words]
+  int hq, hkv, nb, mask_words;
+  int32_t* idx;               // [hkv, nb(nb+1)/2]
+  int32_t* counts;            // [hkv, nb]
+};
+hipError_t launch_union(const UnionLaunch& a, hipStream_t st);
 
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st);

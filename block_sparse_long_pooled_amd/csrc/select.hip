@@ -180,7 +180,48 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
   }
 }
 
+// Group-shared lists: one wave per (query block i, KV group g) ORs the group's
+// per-head mask words covering j <= i and writes the set bits in ascending order
+// (a wave prefix sum of the per-word popcounts gives each word its first slot).
+__global__ __launch_bounds__(64) void union_kernel(UnionLaunch a) {
+  const int i = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int G = a.hq / a.hkv;
+  const int nwords = (i >> 5) + 1;
+  int32_t* out = a.idx + (int64_t)g * ((int64_t)a.nb * (a.nb + 1) / 2) + (int64_t)i * (i + 1) / 2;
+  int base = 0;
+  for (int w0 = 0; w0 < nwords; w0 += 64) {
+    const int wi = w0 + lane;
+    unsigned word = 0;
+    if (wi < nwords && wi < a.mask_words) {
+      for (int hh = 0; hh < G; ++hh) word |= a.mask[((int64_t)(g * G + hh) * a.nb + i) * a.mask_words + wi];
+      if (wi == nwords - 1 && (i & 31) != 31) word &= (2u << (i & 31)) - 1u;  // only j <= i
+    }
+    const int pc = __popc(word);
+    int incl = pc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    int pos = base + incl - pc;
+    while (word != 0u) {
+      const int b = __ffs(word) - 1;
+      out[pos++] = wi * 32 + b;
+      word &= word - 1u;
+    }
+    base += __shfl(incl, 63);
+  }
+  if (lane == 0) a.counts[(int64_t)g * a.nb + i] = base;
+}
+
 }  // namespace
+
+hipError_t launch_union(const UnionLaunch& a, hipStream_t st) {
+  dim3 grid(a.nb, a.hkv);
+  hipLaunchKernelGGL(union_kernel, grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st) {
   SelK p{a, sd};

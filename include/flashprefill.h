@@ -204,6 +204,37 @@ int fp_sparse_attn_masked(const void* q, const void* k, const void* v, int dtype
                           void* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Group-shared lists (a PackGQA-style mode beyond the pages' per-head
+ * selection): one list per KV-head group, the union of the lists of its
+ * hq/hkv query heads, so every head of a group visits the same key blocks in
+ * the same order and the group's K/V tiles are shared in cache.  Each head
+ * attends over a superset of its own list.  Single sequence, packed K/V.
+ *
+ * fp_union_compact -- from the per-head masks of fp_threshold_mask:
+ *   mask   [hq, nb, fp_mask_words(nb)] (only bits j <= i of row i are read)
+ *   idx    out: ascending union of the group's lists per (g, i),
+ *          triangular-packed per group (row i of group g at
+ *          g*nb(nb+1)/2 + i(i+1)/2); capacity fp_idx_capacity(hkv, nb)
+ *   counts out: [hkv, nb] int32
+ *
+ * fp_sparse_attn_grouped -- fp_sparse_attn with idx/counts holding one list
+ *   per KV group (from fp_union_compact): query head h reads the list of
+ *   group h / (hq / hkv).  Other arguments as in fp_sparse_attn.
+ * ------------------------------------------------------------------------- */
+int fp_union_compact(const uint32_t* mask, int nb, int hq, int hkv,
+                     int32_t* idx, int32_t* counts, void* stream);
+
+int fp_sparse_attn_grouped(const void* q, const void* k, const void* v, int dtype,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           int L, int hq, int hkv, int d, int block,
+                           int64_t q_stride_tok, int64_t q_stride_head,
+                           int64_t k_stride_tok, int64_t k_stride_head,
+                           int64_t v_stride_tok, int64_t v_stride_head,
+                           int64_t o_stride_tok, int64_t o_stride_head,
+                           const int32_t* idx, const int32_t* counts, float softmax_scale,
+                           void* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Continuous batching and paged KV (V2 abstract: native paged KV cache and
  * continuous batching).  A batch of n_seqs sequences is packed token-major:
  *

@@ -90,7 +90,7 @@ def attn(name="fp_sparse_attn", **kw):
     a.update(kw)
     args = [a["q"], a["k"], a["v"], a["dtype"], a["qs"], a["ks"], a["vs"], a["L"], a["hq"], a["hkv"], a["d"],
             a["block"], *a["st"]]
-    if name == "fp_sparse_attn":
+    if name in ("fp_sparse_attn", "fp_sparse_attn_grouped"):
         args += [a["idx"], a["cnt"]]
     elif name == "fp_sparse_attn_masked":
         args += [a["idx"]]
@@ -177,6 +177,16 @@ def test_chunked_rejects():
                                     None, 0, 0, 4, 2, 64, 128, 512, 128, 0, 256, 128, 0, 256, 128, 512, 128,
                                     P, P, 0.088, P, None, None)
     assert rc == EUNSUP
+
+
+def test_grouped_rejects():
+    lib = _lib.load()
+    assert lib.fp_union_compact(None, 32, 4, 2, P, P, None) == EINVAL
+    assert lib.fp_union_compact(P + 2, 32, 4, 2, P, P, None) == EINVAL
+    assert lib.fp_union_compact(P, 32, 5, 2, P, P, None) == EINVAL
+    assert lib.fp_union_compact(P, 0, 4, 2, P, P, None) == _lib.FP_OK
+    assert attn("fp_sparse_attn_grouped", idx=None) == EINVAL
+    assert attn("fp_sparse_attn_grouped", d=64) == EUNSUP
 
 
 def test_empty_inputs_are_a_no_op():
