@@ -170,6 +170,43 @@ def time_chunked(r, wl, alpha, chunk, reps=3):
     }
 
 
+def time_grouped(r, wl, alpha, reps=2):
+    """Group-shared lists on the same inputs: per-head masks, their union per KV
+    group, and attention with every head reading its group's list."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    q, k, v, qs, ks, vs, out = r["tensors"]
+    pq, pk = r["pooled"]
+    hq, hkv, d = q.shape[1], k.shape[1], q.shape[2]
+    mask = fp.threshold_mask(pq, pk, alpha, wl.n_sink, wl.n_local)
+    gidx, gcounts = fp.union_compact(mask, hkv)
+    fp.sparse_attn_grouped(q, k, v, gidx, gcounts, qs, ks, vs, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for _ in range(reps):
+        fp.threshold_mask(pq, pk, alpha, wl.n_sink, wl.n_local, mask=mask)
+    ev[1].record()
+    for _ in range(reps):
+        fp.union_compact(mask, hkv, idx=gidx, counts=gcounts)
+    ev[2].record()
+    for _ in range(reps):
+        fp.sparse_attn_grouped(q, k, v, gidx, gcounts, qs, ks, vs, out=out)
+    ev[3].record()
+    torch.cuda.synchronize()
+    nb = r["nb"]
+    group_tiles = int(gcounts.sum().item()) * (hq // hkv)
+    am = ev[2].elapsed_time(ev[3]) / reps
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP8_TFLOPS
+    tf = group_tiles * 4.0 * BLOCK * BLOCK * d / (am * 1e-3) / 1e12
+    return {
+        "threshold_mask_ms": ev[0].elapsed_time(ev[1]) / reps, "union_compact_ms": ev[1].elapsed_time(ev[2]) / reps,
+        "attn_ms": am, "density": group_tiles / (hq * nb * (nb + 1) / 2),
+        "attn_computed_tflops": tf, "mfma_frac": tf / peak,
+    }
+
+
 def time_logical_skip(r, wl, alpha, reps=2):
     """The same selection as a bit-packed mask and the masked loop over every causal
     block (the logical skipping that list compaction replaces)."""
@@ -311,6 +348,11 @@ def main():
             "note": "masked loop over every causal block, same selection; outputs bit-identical",
         }
         log(f"logical-skip attention {am:.2f} ms (lists: {r['attn_ms']:.2f} ms)")
+    if not args.no_ablation:
+        extra["group_shared_lists"] = time_grouped(r, wl, alpha)
+        gs = extra["group_shared_lists"]
+        log(f"group-shared lists: density {gs['density']:.3f}, attention {gs['attn_ms']:.2f} ms "
+            f"({gs['mfma_frac'] * 100:.1f}% of MFMA peak)")
     if not args.no_ablation and wl.L >= 8 * 16384:
         extra["chunked_prefill"] = time_chunked(r, wl, alpha, 16384)
         log(f"chunked prefill (16K of {wl.L}) {extra['chunked_prefill']['ms']:.2f} ms")
