@@ -37,6 +37,11 @@ it is used):
 * varlen/paged: every sequence is processed on its own with queries and keys
   starting at token 0; the page table is addressing only, so it never appears
   here;
+* the V2 "mean correction term" is named but not defined on the pages.  Kept
+  outside the core above as a switchable assumption (``mean_correction``): every
+  causal key block a list leaves out still enters the softmax, as n_j copies of
+  its mean key with its mean value, so the pruned probability mass is restored
+  approximately;
 * group-shared lists (a PackGQA-style mode, beyond what the pages define): the
   list of a KV-head group is the union of its query heads' lists, and every
   query head of the group attends over that union (a superset of its own list);
@@ -70,7 +75,7 @@ __all__ = [
     "keep_mask", "compact", "select_blocks", "attend_block", "sparse_attention",
     "dense_attention", "select_blocks_varlen", "sparse_attention_varlen", "dense_attention_varlen",
     "chunk_blocks", "pool_chunk", "select_blocks_chunked", "sparse_attention_chunked",
-    "select_blocks_grouped",
+    "select_blocks_grouped", "mean_correction",
 ]
 
 
@@ -381,3 +386,43 @@ def select_blocks_grouped(q: np.ndarray, k: np.ndarray, block: int, alpha: float
         gkeep[h // group] |= keep[h]
     lists, counts = compact(gkeep)
     return dict(heads=per_head, keep=gkeep, lists=lists, counts=counts)
+
+
+
+# --------------------------------------- V2 mean correction (an assumption)
+def mean_correction(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists, block: int,
+                    scale: Optional[float] = None, want_lse: bool = False):
+    """ASSUMPTION, not defined on the pages ([V2] abstract only names a mean correction
+    term that suppresses the approximation error).  Reading: sparse attention over the
+    lists, plus every causal block j missing from the list of (h, i) entering the
+    softmax as n_j copies of its mean key kbar_j with its mean value vbar_j:
+
+        O_t = (sum_{c in C(t)} e^{s_tc} v_c + sum_{j pruned} n_j e^{scale q_t.kbar_j} vbar_j)
+              / (sum_{c in C(t)} e^{s_tc} + sum_{j pruned} n_j e^{scale q_t.kbar_j}).
+
+    Pruned blocks lie strictly below the diagonal (the diagonal is always listed), so
+    all their keys are visible to every query of block i."""
+    L, hq, d = q.shape
+    group = hq // k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nb = -(-L // block)
+    kbar, vbar = pool(k, block), pool(v, block)
+    n = np.array([min(block, L - j * block) for j in range(nb)], dtype=np.float64)
+    out = np.empty((L, hq, d), dtype=np.float64)
+    lse = np.empty((hq, L), dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        for i in range(nb):
+            t = np.arange(i * block, min((i + 1) * block, L))
+            kept = np.asarray(lists[h][i], dtype=np.int64)
+            c = np.concatenate([np.arange(j * block, min((j + 1) * block, L)) for j in kept])
+            x = scale * (q[t, h, :] @ k[c, g, :].T)
+            x = np.where(c[None, :] <= t[:, None], x, -np.inf)
+            pruned = np.setdiff1d(np.arange(i + 1), kept)
+            y = scale * (q[t, h, :] @ kbar[g, pruned, :].T) + np.log(n[pruned])[None, :]
+            M = np.maximum(np.max(x, axis=1), np.max(y, axis=1) if pruned.size else -np.inf)[:, None]
+            ex, ey = np.exp(x - M), np.exp(y - M)
+            den = ex.sum(axis=1, keepdims=True) + ey.sum(axis=1, keepdims=True)
+            out[t, h, :] = (ex @ v[c, g, :] + ey @ vbar[g, pruned, :]) / den
+            lse[h, t] = (M + np.log(den))[:, 0]
+    return (out, lse) if want_lse else out

@@ -461,3 +461,69 @@ def test_grouped_alpha_zero_and_above_one():
     j = np.arange(nb)[None, :]
     want = (j <= i) & ((j < 2) | (j > i - 2))
     assert np.array_equal(forced["keep"], np.broadcast_to(want, (2, nb, nb)))
+
+
+
+# --------------------------------------- V2 mean correction (an assumption)
+def test_mean_correction_is_noop_without_pruning():
+    """Full lists: nothing is pruned, so the corrected output is plain attention
+    (torch fp64 SDPA)."""
+    L, block = 4 * 16 + 5, 16
+    q, k, v = rand(L, 4, 8), rand(L, 2, 8), rand(L, 2, 8)
+    nb = -(-L // block)
+    full = [[np.arange(i + 1) for i in range(nb)] for _ in range(4)]
+    out = O.mean_correction(q, k, v, full, block)
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(np.repeat(k, 2, axis=1)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.repeat(v, 2, axis=1)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True).permute(1, 0, 2).numpy()
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_mean_correction_exact_for_constant_blocks():
+    """Closed form: if every block's keys and values are constant inside the block, n_j
+    copies of (kbar_j, vbar_j) are exactly the block, so the corrected sparse output
+    equals dense attention whatever the lists prune (diagonal kept)."""
+    L, block = 5 * 8, 8
+    nb = L // block
+    kb, vb = rand(nb, 2, 6), rand(nb, 2, 6)
+    k = np.repeat(kb, block, axis=0)
+    v = np.repeat(vb, block, axis=0)
+    q = rand(L, 4, 6)
+    rng = np.random.default_rng(5)
+    lists = [[np.array(sorted(set(rng.choice(i + 1, size=rng.integers(1, i + 2), replace=False)) | {i}))
+              for i in range(nb)] for _ in range(4)]
+    out, lse = O.mean_correction(q, k, v, lists, block, want_lse=True)
+    dense, dlse = O.dense_attention(q, k, v, want_lse=True)
+    # pruned blocks lie below the diagonal, so all their keys are visible; the
+    # diagonal block is listed and stays causal on both sides
+    assert np.allclose(out, dense, rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, dlse, rtol=1e-12, atol=1e-12)
+
+
+def test_mean_correction_brute_force():
+    """Tiny case by pure-Python loops over tokens and pruned blocks."""
+    L, block, d = 3 * 4 + 1, 4, 3
+    q, k, v = rand(L, 1, d), rand(L, 1, d), rand(L, 1, d)
+    lists = [[np.array([0]), np.array([1]), np.array([0, 2]), np.array([3])]]
+    out = O.mean_correction(q, k, v, lists, block)
+    sc = 1 / math.sqrt(d)
+    for t in range(L):
+        i = t // block
+        num = [0.0] * d
+        den = 0.0
+        for j in range(i + 1):
+            toks = [c for c in range(j * block, min((j + 1) * block, L))]
+            if j in lists[0][i]:
+                for c in toks:
+                    if c <= t:
+                        w = math.exp(sc * sum(q[t, 0, e] * k[c, 0, e] for e in range(d)))
+                        den += w
+                        num = [num[e] + w * v[c, 0, e] for e in range(d)]
+            else:
+                kbar = [sum(k[c, 0, e] for c in toks) / len(toks) for e in range(d)]
+                vbar = [sum(v[c, 0, e] for c in toks) / len(toks) for e in range(d)]
+                w = len(toks) * math.exp(sc * sum(q[t, 0, e] * kbar[e] for e in range(d)))
+                den += w
+                num = [num[e] + w * vbar[e] for e in range(d)]
+        assert np.allclose(out[t, 0], [x / den for x in num], rtol=1e-12, atol=1e-13)
