@@ -140,6 +140,31 @@ def sparse_attn(q, k, v, idx, counts, q_scale=None, k_scale=None, v_scale=None, 
     return _attn("fp_sparse_attn", q, k, v, idx, counts, q_scale, k_scale, v_scale, softmax_scale, out, return_lse)
 
 
+def pool(x, scale=None, pooled=None):
+    """Block means of x [L, H, 128] (bf16, or e4m3 codes with per-head scale)
+    -> [H, nb, 128] fp64."""
+    L, H, d = x.shape
+    if pooled is None:
+        pooled = torch.empty((H, _nb(L), d), dtype=torch.float64, device=x.device)
+    call("fp_pool", _ptr(x), _dtype_code(x), _ptr(scale), L, H, d, BLOCK, x.stride(0), x.stride(1), _ptr(pooled),
+         _stream(x))
+    return pooled
+
+
+def mean_correct(q, pooled_k, pooled_v, idx, counts, out, lse, q_scale=None, softmax_scale=None):
+    """The V2 mean correction as implemented here (an assumption, off unless called):
+    fold every pruned block, as 128 copies of its mean key and value, into the output
+    and LSE of sparse_attn(..., return_lse=True), in place."""
+    L, hq, d = q.shape
+    hkv = pooled_k.shape[0]
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    call("fp_mean_correct", _ptr(q), _dtype_code(q), _ptr(q_scale), _ptr(pooled_k), _ptr(pooled_v), L, hq, hkv,
+         d, BLOCK, q.stride(0), q.stride(1), out.stride(0), out.stride(1), _ptr(idx), _ptr(counts),
+         float(softmax_scale), _ptr(out), _ptr(lse), _stream(q))
+    return out, lse
+
+
 def union_compact(mask, hkv: int, idx=None, counts=None):
     """Group-shared lists: the union of the per-head masks (from threshold_mask) of
     every KV group, as ascending lists -> (idx [hkv * nb(nb+1)/2] int32,

@@ -45,6 +45,9 @@ _SIGNATURES = {
     "fp_threshold_mask": (c_int, [_p, _p, c_int, c_int, c_int, c_int, c_double, c_double, c_int, c_int, _p, _p]),
     "fp_sparse_attn_masked": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                       _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, c_float, _p, _p, _p]),
+    "fp_pool": (c_int, [_p, c_int, _p, c_int, c_int, c_int, c_int, _i64, _i64, _p, _p]),
+    "fp_mean_correct": (c_int, [_p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
+                                _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),
     "fp_union_compact": (c_int, [_p, c_int, c_int, c_int, _p, _p, _p]),
     "fp_sparse_attn_grouped": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                        _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),

@@ -12,7 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "pool.hip", "select.hip", "attn.hip"]
+SOURCES = ["api.hip", "pool.hip", "select.hip", "attn.hip", "meancorr.hip"]
 LIB_NAME = "libflashprefill.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -310,6 +310,50 @@ static int attn_common(const void* q, const void* k, const void* v, int dtype, c
   return launch_status(fp::launch_attn(a, sd, pd, (hipStream_t)stream));
 }
 
+int fp_pool(const void* x, int dtype, const float* scale, int L, int H, int d, int block,
+            int64_t stride_tok, int64_t stride_head, double* pooled, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, H, H, d, block))) return r;
+  if (L < 0) return fail(FP_EINVAL, "L < 0");
+  if (L == 0) return ok();
+  if ((r = check_tensor("x", x, dtype, stride_tok, stride_head))) return r;
+  if (pooled == nullptr) return fail(FP_EINVAL, "pooled output is NULL");
+  if (!aligned16(pooled)) return fail(FP_EINVAL, "pooled output not 16-byte aligned");
+  if (dtype == FP_FP8_E4M3 && scale == nullptr) return fail(FP_EINVAL, "fp8 needs a per-head scale");
+  fp::SeqDesc sd = single_seq(L);
+  fp::PageDesc pd{nullptr, 0, 0};
+  fp::PoolLaunch a{};
+  a.query_view = false;
+  a.dtype = dtype;
+  a.x = x; a.scale = scale; a.H = H; a.st_page = 0; a.st_tok = stride_tok; a.st_head = stride_head; a.paged = false;
+  a.out = pooled;
+  return launch_status(fp::launch_pool(a, sd, pd, (hipStream_t)stream));
+}
+
+int fp_mean_correct(const void* q, int dtype, const float* q_scale,
+                    const double* pooled_k, const double* pooled_v,
+                    int L, int hq, int hkv, int d, int block,
+                    int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                    const int32_t* idx, const int32_t* counts, float softmax_scale,
+                    void* out, float* lse, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
+  if (L < 0) return fail(FP_EINVAL, "L < 0");
+  if (L == 0) return ok();
+  if ((r = check_tensor("q", q, dtype, q_stride_tok, q_stride_head))) return r;
+  if ((r = check_tensor("out", out, FP_BF16, o_stride_tok, o_stride_head))) return r;
+  if (pooled_k == nullptr || pooled_v == nullptr) return fail(FP_EINVAL, "pooled K/V is NULL");
+  if (idx == nullptr || counts == nullptr) return fail(FP_EINVAL, "idx/counts is NULL");
+  if (lse == nullptr) return fail(FP_EINVAL, "lse is NULL (the correction needs the sparse LSE)");
+  if ((uintptr_t)lse & 3u) return fail(FP_EINVAL, "lse not 4-byte aligned");
+  if (dtype == FP_FP8_E4M3 && q_scale == nullptr) return fail(FP_EINVAL, "fp8 needs q_scale");
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f) return fail(FP_EINVAL, "softmax_scale must be > 0");
+  if ((int64_t)hq * nblocks(L) >= (int64_t)1 << 31) return fail(FP_EINVAL, "grid too large");
+  fp::MeanCorrLaunch a{q, q_scale, dtype, L, hq, hkv, q_stride_tok, q_stride_head, o_stride_tok, o_stride_head,
+                       pooled_k, pooled_v, idx, counts, softmax_scale, out, lse};
+  return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
+}
+
 int fp_union_compact(const uint32_t* mask, int nb, int hq, int hkv, int32_t* idx, int32_t* counts, void* stream) {
   if (hq < 1 || hkv < 1 || hq % hkv != 0) return fail(FP_EINVAL, "hq=%d must be a positive multiple of hkv=%d", hq, hkv);
   if (nb < 0 || nb > (1 << 24)) return fail(FP_EINVAL, "nb=%d out of range", nb);

@@ -91,6 +91,24 @@ struct UnionLaunch {
 };
 hipError_t launch_union(const UnionLaunch& a, hipStream_t st);
 
+// V2 mean correction (an assumption): fold the pruned blocks' pooled means into a
+// sparse attention result, in place.
+struct MeanCorrLaunch {
+  const void* q;
+  const float* q_scale;
+  int dtype;
+  int L, hq, hkv;
+  int64_t q_st, q_sh, o_st, o_sh;
+  const double* pooled_k;     // [hkv, nb, d]
+  const double* pooled_v;     // [hkv, nb, d]
+  const int32_t* idx;         // per-head lists of the sparse call
+  const int32_t* counts;
+  float softmax_scale;
+  void* out;                  // bf16 [L, hq, d], in and out
+  float* lse;                 // [hq, L], in and out
+};
+hipError_t launch_meancorr(const MeanCorrLaunch& a, hipStream_t st);
+
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st);
 hipError_t launch_attn(const AttnLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);

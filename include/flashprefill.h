@@ -204,6 +204,37 @@ int fp_sparse_attn_masked(const void* q, const void* k, const void* v, int dtype
                           void* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * fp_pool -- block mean pooling of any tensor x [L, H, d] (as fp_discover does
+ * for Q and K): pooled [H, nb, d] fp64, fp8 inputs scaled per head.  Used to pool
+ * V for the mean correction below.
+ * ------------------------------------------------------------------------- */
+int fp_pool(const void* x, int dtype, const float* scale, int L, int H, int d, int block,
+            int64_t stride_tok, int64_t stride_head, double* pooled, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * fp_mean_correct -- the FlashPrefill V2 "mean correction term", which the V2
+ * abstract names without defining.  This is an ASSUMPTION, off unless called:
+ * every causal key block that the list of (h, i) prunes (all lie below the
+ * diagonal) still enters the softmax as 128 copies of its mean key with its mean
+ * value:
+ *     O' = (Z O + sum_j 128 e^{s_j} vbar_j) / (Z + sum_j 128 e^{s_j}),
+ *     s_j = softmax_scale * q . kbar_j,  Z = e^{LSE},
+ * applied in place to the output and LSE of an fp_sparse_attn call.
+ *   pooled_k   [hkv, nb, d] fp64 (from fp_discover)
+ *   pooled_v   [hkv, nb, d] fp64 (from fp_pool on V)
+ *   idx/counts the per-head lists the sparse call used
+ *   out, lse   in: the sparse output and LSE; out: corrected
+ * Single sequence.  Other arguments as in fp_sparse_attn.
+ * ------------------------------------------------------------------------- */
+int fp_mean_correct(const void* q, int dtype, const float* q_scale,
+                    const double* pooled_k, const double* pooled_v,
+                    int L, int hq, int hkv, int d, int block,
+                    int64_t q_stride_tok, int64_t q_stride_head,
+                    int64_t o_stride_tok, int64_t o_stride_head,
+                    const int32_t* idx, const int32_t* counts, float softmax_scale,
+                    void* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Group-shared lists (a PackGQA-style mode beyond the pages' per-head
  * selection): one list per KV-head group, the union of the lists of its
  * hq/hkv query heads, so every head of a group visits the same key blocks in

@@ -189,6 +189,22 @@ def test_grouped_rejects():
     assert attn("fp_sparse_attn_grouped", d=64) == EUNSUP
 
 
+def test_pool_and_mean_correct_reject():
+    lib = _lib.load()
+    assert lib.fp_pool(None, 0, None, 256, 2, 128, 128, 256, 128, P, None) == EINVAL
+    assert lib.fp_pool(P, 1, None, 256, 2, 128, 128, 256, 128, P, None) == EINVAL  # fp8 without scale
+    assert lib.fp_pool(P, 0, None, 256, 2, 64, 128, 256, 128, P, None) == EUNSUP
+    assert lib.fp_pool(P, 0, None, 0, 2, 128, 128, 256, 128, P, None) == _lib.FP_OK
+    args = [P, 0, None, P, P, 1024, 4, 2, 128, 128, 512, 128, 512, 128, P, P, 0.088, P, P, None]
+    # the pointers are fake, so only reject paths are exercised
+    bad_lse = list(args); bad_lse[18] = None
+    assert lib.fp_mean_correct(*bad_lse) == EINVAL and b"lse" in lib.fp_last_error()
+    bad_pk = list(args); bad_pk[3] = None
+    assert lib.fp_mean_correct(*bad_pk) == EINVAL
+    bad_d = list(args); bad_d[8] = 96
+    assert lib.fp_mean_correct(*bad_d) == EUNSUP
+
+
 def test_empty_inputs_are_a_no_op():
     """L = 0 validates and returns FP_OK without launching anything."""
     assert discover(L=0) == _lib.FP_OK

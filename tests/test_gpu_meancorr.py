@@ -1,0 +1,59 @@
+"""The V2 mean correction, GPU side (an assumption kept outside the oracle-checked
+core; its definition is oracle.mean_correction): pooled V is bit-exact; the
+corrected output and LSE match the oracle's definition over the GPU's own lists;
+with nothing pruned (alpha = 0) the pass leaves output and LSE unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_pooled_amd as fp
+import oracle as O
+from helpers import TOL_BF16, TOL_FP8, oracle_inputs, to_device, unpack_lists
+from test_gpu_parity import workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.mark.parametrize("name", ["gqa_ragged", "fp8_ragged"])
+def test_pool_v_bit_exact(name):
+    wl = workload(name)
+    print(f"[case] pool V {name}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
+    pv = fp.pool(v, vs)
+    torch.cuda.synchronize()
+    _, _, ov = oracle_inputs(wl)
+    assert np.array_equal(pv.cpu().numpy(), O.pool(ov, 128))
+
+
+@pytest.mark.parametrize("name,alpha", [("tiny", 0.1), ("gqa_ragged", 0.3), ("fp8_ragged", 0.1), ("gqa7", 0.2)])
+def test_mean_correction_matches_definition(name, alpha):
+    wl = workload(name)
+    print(f"[case] mean correction {name} alpha={alpha}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
+    pq, pk = fp.discover(q, k, qs, ks)
+    pv = fp.pool(v, vs)
+    idx, counts = fp.threshold_compact(pq, pk, alpha, wl.n_sink, wl.n_local)
+    out, lse = fp.sparse_attn(q, k, v, idx, counts, qs, ks, vs, return_lse=True)
+    fp.mean_correct(q, pk, pv, idx, counts, out, lse, q_scale=qs)
+    torch.cuda.synchronize()
+    nb = -(-wl.L // 128)
+    lists = [unpack_lists(idx.cpu().numpy(), counts.cpu().numpy(), h, nb, nb * (nb + 1) // 2) for h in range(wl.hq)]
+    oq, ok_, ov = oracle_inputs(wl)
+    ref, ref_lse = O.mean_correction(oq, ok_, ov, lists, 128, want_lse=True)
+    tol = TOL_BF16 if wl.dtype == "bf16" else TOL_FP8
+    assert np.max(np.abs(out.float().cpu().numpy() - ref)) <= tol
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-3 * max(1.0, np.abs(ref_lse).max())
+
+
+def test_mean_correction_is_noop_without_pruning():
+    wl = workload("gqa_ragged")
+    print(f"[case] mean correction alpha=0 L={wl.L}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
+    pq, pk = fp.discover(q, k, qs, ks)
+    pv = fp.pool(v, vs)
+    idx, counts = fp.threshold_compact(pq, pk, 0.0, wl.n_sink, wl.n_local)
+    out, lse = fp.sparse_attn(q, k, v, idx, counts, qs, ks, vs, return_lse=True)
+    o2, l2 = out.clone(), lse.clone()
+    fp.mean_correct(q, pk, pv, idx, counts, o2, l2, q_scale=qs)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
