@@ -124,6 +124,7 @@ def time_hot_path(wl, steps, warmup, alpha):
     res["counts"] = counts
     res["tensors"] = (q, k, v, qs, ks, vs, out)
     res["pooled"] = (pq, pk)
+    res["lists"] = (idx, counts)
     return res
 
 
@@ -205,6 +206,48 @@ def time_grouped(r, wl, alpha, reps=2):
         "attn_ms": am, "density": group_tiles / (hq * nb * (nb + 1) / 2),
         "attn_computed_tflops": tf, "mfma_frac": tf / peak,
     }
+
+
+def time_mean_correction(r, wl, alpha, reps=2):
+    """The V2 mean correction as implemented here (an assumption): its time, and the
+    relative Frobenius error of the sparse and of the corrected output against the
+    dense kernel on the same inputs."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    q, k, v, qs, ks, vs, _ = r["tensors"]
+    pq, pk = r["pooled"]
+    idx, counts = r["lists"]
+    pv = fp.pool(v, vs)
+    o_s, lse = fp.sparse_attn(q, k, v, idx, counts, qs, ks, vs, return_lse=True)
+    o_c, l_c = o_s.clone(), lse.clone()
+    fp.mean_correct(q, pk, pv, idx, counts, o_c, l_c, q_scale=qs)
+    o_d = fp.dense_attn(q, k, v, qs, ks, vs)
+    torch.cuda.synchronize()
+
+    def rel(a):
+        num = den = 0.0
+        for h0 in range(0, q.shape[1], 4):  # in head slices to bound the fp32 temporaries
+            d = o_d[:, h0:h0 + 4].float()
+            num += float(((a[:, h0:h0 + 4].float() - d) ** 2).sum())
+            den += float((d ** 2).sum())
+        return (num / den) ** 0.5
+    e_s, e_c = rel(o_s), rel(o_c)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        fp.pool(v, vs, pooled=pv)
+    ev[1].record()
+    for _ in range(reps):
+        o_c.copy_(o_s)
+        l_c.copy_(lse)
+        fp.mean_correct(q, pk, pv, idx, counts, o_c, l_c, q_scale=qs)
+    ev[2].record()
+    torch.cuda.synchronize()
+    del o_s, o_c, o_d, lse, l_c
+    return {"pool_v_ms": ev[0].elapsed_time(ev[1]) / reps, "correct_ms_incl_copy": ev[1].elapsed_time(ev[2]) / reps,
+            "rel_err_sparse_vs_dense": e_s, "rel_err_corrected_vs_dense": e_c,
+            "note": "assumption: pruned blocks enter the softmax as 128 copies of their mean key/value"}
 
 
 def time_logical_skip(r, wl, alpha, reps=2):
@@ -353,10 +396,15 @@ def main():
         gs = extra["group_shared_lists"]
         log(f"group-shared lists: density {gs['density']:.3f}, attention {gs['attn_ms']:.2f} ms "
             f"({gs['mfma_frac'] * 100:.1f}% of MFMA peak)")
+    if not args.no_ablation:
+        extra["mean_correction"] = time_mean_correction(r, wl, alpha)
+        mc = extra["mean_correction"]
+        log(f"mean correction {mc['correct_ms_incl_copy']:.2f} ms; rel. error vs dense: sparse "
+            f"{mc['rel_err_sparse_vs_dense']:.4f}, corrected {mc['rel_err_corrected_vs_dense']:.4f}")
     if not args.no_ablation and wl.L >= 8 * 16384:
         extra["chunked_prefill"] = time_chunked(r, wl, alpha, 16384)
         log(f"chunked prefill (16K of {wl.L}) {extra['chunked_prefill']['ms']:.2f} ms")
-    del r["tensors"], r["pooled"]
+    del r["tensors"], r["pooled"], r["lists"]
 
     if not args.no_extra and args.config == 2:
         import torch
@@ -374,7 +422,7 @@ def main():
             "attn_computed_tflops": c8 / (r8["attn_ms"] * 1e-3) / 1e12,
             "mfma_frac_fp8": c8 / (r8["attn_ms"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
         }
-        del r8["tensors"], r8["pooled"], wl8
+        del r8["tensors"], r8["pooled"], r8["lists"], wl8
         log(f"fp8 256K step {extra['fp8_256k']['ms_per_step']:.2f} ms")
 
     line = {
