@@ -93,13 +93,21 @@ __device__ inline void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// MASKED: the logical-skip ablation (FlashPrefill Method 3 contrasts it with
-// physical jumps): the loop visits every causal block j <= i, tests bit j of the
-// row's block mask and branches past unselected blocks.  It cannot start the next
-// selected block's loads before it has found that block, so each selected block
-// waits for its first half tile.
-template <int DT, bool PAGED, bool DENSE, bool LSE, bool MASKED = false>
+// Modes (separate instances, so each workload has its own kernel):
+//   kPrefill  per-head lists, queries = keys of each sequence;
+//   kMasked   the logical-skip ablation (FlashPrefill Method 3 contrasts it with
+//             physical jumps): the loop visits every causal block j <= i, tests
+//             bit j of the row's block mask and branches past unselected blocks.
+//             It cannot start the next selected block's loads before it has found
+//             that block, so each selected block waits for its first half tile;
+//   kGrouped  one list per KV group, read by every query head of the group;
+//   kChunked  chunked / prefix-cached prefill: queries are the last positions of
+//             each sequence, query blocks follow absolute positions.
+enum { kPrefill = 0, kMasked = 1, kGrouped = 2, kChunked = 3 };
+
+template <int DT, bool PAGED, bool DENSE, bool LSE, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
+  constexpr bool MASKED = MODE == kMasked;
   constexpr int ES = DT == 0 ? 2 : 1;             // element size in bytes
   constexpr int ROW = kHeadDim * ES;              // bytes of one K/V row: 256 (bf16), 128 (fp8)
   constexpr int CPR = ROW / 16;                   // 16-byte chunks per row
@@ -128,7 +136,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   const int rest = id / a.hq;
   const int s = rest % p.sd.n_seqs;
   const int r = p.sd.max_nq - 1 - rest / p.sd.n_seqs;  // heaviest query blocks first
-  const SeqPos sp = seq_pos(p.sd, s);
+  SeqPos sp = seq_pos(p.sd, s);
+  if (MODE != kChunked) {  // queries = keys: let the compiler drop the offset arithmetic
+    sp.qtok0 = sp.tok0; sp.qlen = sp.len; sp.qoff = 0; sp.I0 = 0; sp.qblk0 = sp.blk0;
+  }
   if (r < 0 || r >= sp.nq || sp.qblk0 + r >= p.sd.total_qblocks) return;
   // query block r of the sequence is absolute block i: its rows are positions
   // 128i .. 128i+127, of which the query chunk holds [qoff, qoff + qlen)
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   if (DENSE || MASKED) {
     cnt = i + 1;
   } else {
-    const int hl = h / a.list_div;  // the list this head reads (per head, or per KV group)
+    const int hl = MODE == kGrouped ? h / a.list_div : h;  // the list this head reads
     cnt = ((cint_ptr)a.counts)[(int64_t)hl * p.sd.total_qblocks + sp.qblk0 + r];
     cnt = uniform(cnt < 0 ? 0 : (cnt > i + 1 ? i + 1 : cnt));
     // rows I0 .. i-1 of the sequence hold I0+1 .. i slots
@@ -512,27 +523,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   }
 }
 
-template <int DT>
-void launch_masked(const AttnK& p, dim3 grid, hipStream_t st) {
-  if (p.a.lse != nullptr)
-    hipLaunchKernelGGL((attn_kernel<DT, false, false, true, true>), grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((attn_kernel<DT, false, false, false, true>), grid, dim3(kThreads), 0, st, p);
-}
-
-template <int DT, bool PAGED, bool DENSE>
+template <int DT, bool PAGED, bool DENSE, int MODE>
 void launch_l(const AttnK& p, dim3 grid, hipStream_t st) {
   if (p.a.lse != nullptr)
-    hipLaunchKernelGGL((attn_kernel<DT, PAGED, DENSE, true>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<DT, PAGED, DENSE, true, MODE>), grid, dim3(kThreads), 0, st, p);
   else
-    hipLaunchKernelGGL((attn_kernel<DT, PAGED, DENSE, false>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((attn_kernel<DT, PAGED, DENSE, false, MODE>), grid, dim3(kThreads), 0, st, p);
 }
 
-template <int DT, bool PAGED>
-hipError_t launch_t(const AttnK& p, dim3 grid, hipStream_t st) {
-  if (p.a.idx == nullptr) launch_l<DT, PAGED, true>(p, grid, st);
-  else launch_l<DT, PAGED, false>(p, grid, st);
-  return hipGetLastError();
+template <int DT, bool PAGED, int MODE>
+void launch_t(const AttnK& p, dim3 grid, hipStream_t st) {
+  if (p.a.idx == nullptr) launch_l<DT, PAGED, true, MODE>(p, grid, st);
+  else launch_l<DT, PAGED, false, MODE>(p, grid, st);
+}
+
+template <int DT>
+void launch_dt(const AttnK& p, const PageDesc& pd, dim3 grid, hipStream_t st) {
+  const bool paged = pd.table != nullptr;
+  if (p.a.mask != nullptr) launch_l<DT, false, false, kMasked>(p, grid, st);
+  else if (p.a.list_div > 1) launch_l<DT, false, false, kGrouped>(p, grid, st);
+  else if (p.sd.cu_seqlens_q != nullptr) {
+    if (paged) launch_t<DT, true, kChunked>(p, grid, st);
+    else launch_t<DT, false, kChunked>(p, grid, st);
+  } else {
+    if (paged) launch_t<DT, true, kPrefill>(p, grid, st);
+    else launch_t<DT, false, kPrefill>(p, grid, st);
+  }
 }
 
 }  // namespace
@@ -541,14 +557,9 @@ hipError_t launch_attn(const AttnLaunch& a, const SeqDesc& sd, const PageDesc& p
   AttnK p{a, sd, pd, a.hq / a.hkv};
   const int64_t n_wg = (int64_t)a.hq * sd.max_nq * sd.n_seqs;
   dim3 grid((unsigned)n_wg);
-  const bool paged = pd.table != nullptr;
-  if (a.mask != nullptr) {
-    if (a.dtype == 0) launch_masked<0>(p, grid, st);
-    else launch_masked<1>(p, grid, st);
-    return hipGetLastError();
-  }
-  if (a.dtype == 0) return paged ? launch_t<0, true>(p, grid, st) : launch_t<0, false>(p, grid, st);
-  return paged ? launch_t<1, true>(p, grid, st) : launch_t<1, false>(p, grid, st);
+  if (a.dtype == 0) launch_dt<0>(p, pd, grid, st);
+  else launch_dt<1>(p, pd, grid, st);
+  return hipGetLastError();
 }
 
 }  // namespace fp
