@@ -151,17 +151,28 @@ def pool(x, scale=None, pooled=None):
     return pooled
 
 
-def mean_correct(q, pooled_k, pooled_v, idx, counts, out, lse, q_scale=None, softmax_scale=None):
+def mean_correct_workspace(L: int, hkv: int, device) -> torch.Tensor:
+    """Scratch for mean_correct: fp_mean_correct_workspace_bytes(L, hkv) bytes."""
+    n = int(load().fp_mean_correct_workspace_bytes(L, hkv))
+    if n < 0:
+        raise ValueError(f"invalid L={L} / hkv={hkv}")
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def mean_correct(q, pooled_k, pooled_v, idx, counts, out, lse, q_scale=None, softmax_scale=None, workspace=None):
     """The V2 mean correction as implemented here (an assumption, off unless called):
     fold every pruned block, as 128 copies of its mean key and value, into the output
-    and LSE of sparse_attn(..., return_lse=True), in place."""
+    and LSE of sparse_attn(..., return_lse=True), in place.  workspace: a buffer from
+    mean_correct_workspace (allocated here when None)."""
     L, hq, d = q.shape
     hkv = pooled_k.shape[0]
     if softmax_scale is None:
         softmax_scale = default_scale(d)
+    if workspace is None:
+        workspace = mean_correct_workspace(L, hkv, q.device)
     call("fp_mean_correct", _ptr(q), _dtype_code(q), _ptr(q_scale), _ptr(pooled_k), _ptr(pooled_v), L, hq, hkv,
          d, BLOCK, q.stride(0), q.stride(1), out.stride(0), out.stride(1), _ptr(idx), _ptr(counts),
-         float(softmax_scale), _ptr(out), _ptr(lse), _stream(q))
+         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q))
     return out, lse
 
 

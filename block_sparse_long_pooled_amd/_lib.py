@@ -47,7 +47,8 @@ _SIGNATURES = {
                                       _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, c_float, _p, _p, _p]),
     "fp_pool": (c_int, [_p, c_int, _p, c_int, c_int, c_int, c_int, _i64, _i64, _p, _p]),
     "fp_mean_correct": (c_int, [_p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
-                                _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),
+                                _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p, _i64, _p]),
+    "fp_mean_correct_workspace_bytes": (c_int64, [c_int, c_int]),
     "fp_union_compact": (c_int, [_p, c_int, c_int, c_int, _p, _p, _p]),
     "fp_sparse_attn_grouped": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                        _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),

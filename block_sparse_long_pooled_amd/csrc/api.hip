@@ -330,27 +330,39 @@ int fp_pool(const void* x, int dtype, const float* scale, int L, int H, int d, i
   return launch_status(fp::launch_pool(a, sd, pd, (hipStream_t)stream));
 }
 
+int64_t fp_mean_correct_workspace_bytes(int L, int hkv) {
+  if (L < 0 || hkv < 1) return -1;
+  return fp::meancorr_workspace_bytes(L, hkv);
+}
+
 int fp_mean_correct(const void* q, int dtype, const float* q_scale,
                     const double* pooled_k, const double* pooled_v,
                     int L, int hq, int hkv, int d, int block,
                     int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
                     const int32_t* idx, const int32_t* counts, float softmax_scale,
-                    void* out, float* lse, void* stream) {
+                    void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
   int r;
   if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
   if (L < 0) return fail(FP_EINVAL, "L < 0");
   if (L == 0) return ok();
   if ((r = check_tensor("q", q, dtype, q_stride_tok, q_stride_head))) return r;
+  if (workspace == nullptr || !aligned16(workspace)) return fail(FP_EINVAL, "workspace is NULL or not 16-byte aligned");
+  if (workspace_bytes < fp::meancorr_workspace_bytes(L, hkv))
+    return fail(FP_EINVAL, "workspace of %lld bytes < fp_mean_correct_workspace_bytes = %lld",
+                (long long)workspace_bytes, (long long)fp::meancorr_workspace_bytes(L, hkv));
   if ((r = check_tensor("out", out, FP_BF16, o_stride_tok, o_stride_head))) return r;
   if (pooled_k == nullptr || pooled_v == nullptr) return fail(FP_EINVAL, "pooled K/V is NULL");
+  if (!aligned16(pooled_k) || !aligned16(pooled_v)) return fail(FP_EINVAL, "pooled K/V not 16-byte aligned");
   if (idx == nullptr || counts == nullptr) return fail(FP_EINVAL, "idx/counts is NULL");
   if (lse == nullptr) return fail(FP_EINVAL, "lse is NULL (the correction needs the sparse LSE)");
+  if (nblocks(L) > fp::meancorr_max_blocks())
+    return fail(FP_EUNSUPPORTED, "L=%d exceeds the mean correction's %d blocks", L, fp::meancorr_max_blocks());
   if ((uintptr_t)lse & 3u) return fail(FP_EINVAL, "lse not 4-byte aligned");
   if (dtype == FP_FP8_E4M3 && q_scale == nullptr) return fail(FP_EINVAL, "fp8 needs q_scale");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f) return fail(FP_EINVAL, "softmax_scale must be > 0");
   if ((int64_t)hq * nblocks(L) >= (int64_t)1 << 31) return fail(FP_EINVAL, "grid too large");
   fp::MeanCorrLaunch a{q, q_scale, dtype, L, hq, hkv, q_stride_tok, q_stride_head, o_stride_tok, o_stride_head,
-                       pooled_k, pooled_v, idx, counts, softmax_scale, out, lse};
+                       pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, workspace};
   return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
 }
 

@@ -45,25 +45,15 @@ struct AttnK {
   int group;
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 
-// s_waitcnt immediate (gfx9 layout) that waits until at most n vector-memory
-// operations are outstanding and leaves the other counters unconstrained.
-constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Buffer resource over [base, base + nbytes): loads at byte offsets past nbytes
-// return zero, which zero-fills rows past a sequence end without branches.
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
-}
 // voff is per lane, soff wave-uniform (the instruction's scalar offset).
 __device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff = 0) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
@@ -81,16 +71,6 @@ __device__ __attribute__((always_inline)) inline s16x4 lds_tr16(const unsigned c
 }
 __device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const unsigned char* __restrict__ base, unsigned off) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(base + off));
-}
-
-// Workgroup barrier that does not drain the tile loads in flight: only this
-// wave's LDS reads/writes must be complete (lgkmcnt), the asm statements keep
-// the compiler from moving memory operations across it.
-__device__ inline void wg_barrier() {
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(15 << 8));  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Modes (separate instances, so each workload has its own kernel):

@@ -114,6 +114,28 @@ __device__ inline SeqPos seq_pos(const SeqDesc& sd, int s) {
   return p;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate (gfx9 layout) that waits until at most n vector-memory
+// operations are outstanding and leaves the other counters unconstrained.
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Buffer resource over [base, base + nbytes): loads at byte offsets past nbytes
+// return zero, which zero-fills rows past a sequence end without branches.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, unsigned nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+
+// Workgroup barrier that does not drain the direct-to-LDS loads in flight: only
+// this wave's LDS reads/writes must be complete (lgkmcnt), the asm statements keep
+// the compiler from moving memory operations across it.
+__device__ inline void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(63) & ~(15 << 8));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Value of the partner lane l ^ 32 (v_permlane32_swap returns the pair
 // {own, partner} in an order that depends on the half, so callers only use
 // symmetric combinations of the two).

@@ -106,8 +106,11 @@ struct MeanCorrLaunch {
   float softmax_scale;
   void* out;                  // bf16 [L, hq, d], in and out
   float* lse;                 // [hq, L], in and out
+  void* workspace;            // meancorr_workspace_bytes(L, hkv) bytes, 16-byte aligned
 };
 hipError_t launch_meancorr(const MeanCorrLaunch& a, hipStream_t st);
+int meancorr_max_blocks();  // longest row the mean correction handles (blocks)
+int64_t meancorr_workspace_bytes(int L, int hkv);
 
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st);

@@ -223,8 +223,18 @@ int fp_pool(const void* x, int dtype, const float* scale, int L, int H, int d, i
  *   pooled_k   [hkv, nb, d] fp64 (from fp_discover)
  *   pooled_v   [hkv, nb, d] fp64 (from fp_pool on V)
  *   idx/counts the per-head lists the sparse call used
- *   out, lse   in: the sparse output and LSE; out: corrected
- * Single sequence.  Other arguments as in fp_sparse_attn.
+ *   out, lse   in: the sparse output and LSE; out: corrected (rows with
+ *              nothing pruned are left untouched)
+ *   workspace  caller-owned device scratch of at least
+ *              fp_mean_correct_workspace_bytes(L, hkv) bytes (16-byte aligned;
+ *              3 MB at L = 128K, hkv = 4): the means converted once per KV head
+ *              into bf16 tile images.  Its contents are overwritten; calls that
+ *              share one workspace must not overlap.  NULL, misaligned or too
+ *              small: FP_EINVAL.
+ * Single sequence of at most 65536 blocks (longer: FP_EUNSUPPORTED); pooled
+ * K/V 16-byte aligned (else FP_EINVAL).  Numerics: logits from the fp64 means
+ * split into two bf16 terms (~2^-17 relative), the correction's values and
+ * weights in bf16 with fp32 accumulation.  Other arguments as in fp_sparse_attn.
  * ------------------------------------------------------------------------- */
 int fp_mean_correct(const void* q, int dtype, const float* q_scale,
                     const double* pooled_k, const double* pooled_v,
@@ -232,7 +242,12 @@ int fp_mean_correct(const void* q, int dtype, const float* q_scale,
                     int64_t q_stride_tok, int64_t q_stride_head,
                     int64_t o_stride_tok, int64_t o_stride_head,
                     const int32_t* idx, const int32_t* counts, float softmax_scale,
-                    void* out, float* lse, void* stream);
+                    void* out, float* lse, void* workspace, int64_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes fp_mean_correct needs for L tokens and hkv KV heads
+ * (-1 for L < 0 or hkv < 1).  Host only. */
+int64_t fp_mean_correct_workspace_bytes(int L, int hkv);
 
 /* ---------------------------------------------------------------------------
  * Group-shared lists (a PackGQA-style mode beyond the pages' per-head

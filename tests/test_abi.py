@@ -195,14 +195,26 @@ def test_pool_and_mean_correct_reject():
     assert lib.fp_pool(P, 1, None, 256, 2, 128, 128, 256, 128, P, None) == EINVAL  # fp8 without scale
     assert lib.fp_pool(P, 0, None, 256, 2, 64, 128, 256, 128, P, None) == EUNSUP
     assert lib.fp_pool(P, 0, None, 0, 2, 128, 128, 256, 128, P, None) == _lib.FP_OK
-    args = [P, 0, None, P, P, 1024, 4, 2, 128, 128, 512, 128, 512, 128, P, P, 0.088, P, P, None]
+    ws = lib.fp_mean_correct_workspace_bytes(1024, 2)
+    assert ws == 2 * 1 * 3 * 32 * 256  # 2 KV heads x 1 tile of 32 pooled keys x 24 KB
+    assert lib.fp_mean_correct_workspace_bytes(-1, 2) == -1 and lib.fp_mean_correct_workspace_bytes(1024, 0) == -1
+    args = [P, 0, None, P, P, 1024, 4, 2, 128, 128, 512, 128, 512, 128, P, P, 0.088, P, P, P, ws, None]
     # the pointers are fake, so only reject paths are exercised
     bad_lse = list(args); bad_lse[18] = None
     assert lib.fp_mean_correct(*bad_lse) == EINVAL and b"lse" in lib.fp_last_error()
     bad_pk = list(args); bad_pk[3] = None
     assert lib.fp_mean_correct(*bad_pk) == EINVAL
+    bad_pk = list(args); bad_pk[4] = P + 8
+    assert lib.fp_mean_correct(*bad_pk) == EINVAL and b"aligned" in lib.fp_last_error()
     bad_d = list(args); bad_d[8] = 96
     assert lib.fp_mean_correct(*bad_d) == EUNSUP
+    bad_ws = list(args); bad_ws[19] = None
+    assert lib.fp_mean_correct(*bad_ws) == EINVAL and b"workspace" in lib.fp_last_error()
+    bad_ws = list(args); bad_ws[20] = ws - 1
+    assert lib.fp_mean_correct(*bad_ws) == EINVAL and b"workspace" in lib.fp_last_error()
+    too_long = list(args); too_long[5] = 65536 * 128 + 1
+    too_long[20] = lib.fp_mean_correct_workspace_bytes(too_long[5], 2)
+    assert lib.fp_mean_correct(*too_long) == EUNSUP
 
 
 def test_empty_inputs_are_a_no_op():
