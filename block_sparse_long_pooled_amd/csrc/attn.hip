@@ -4,12 +4,9 @@
 // paged KV cache, continuous batching).
 //
 // CDNA4 design (not the H20 one on the pages):
-//   * one workgroup = one (query head, query block of 128 tokens), 8 waves and
-//     one workgroup per CU, so the K/V tiles can be double-buffered in LDS
-//     (2 x 74 KB);
-//   * wave w takes query rows 32*(w%4).. +31 against keys 64*(w/4).. +63 of every
-//     tile: the two waves of a row group keep separate online-softmax states over
-//     disjoint key halves and merge them once, after the last tile;
+//   * one workgroup = one (query head, query block of 128 tokens), 4 waves of 32
+//     query rows, two workgroups per CU (they take turns on the matrix cores the
+//     way ping-pong warpgroups do on Hopper);
 //   * the transposed products S^T = K Q^T and O^T = V^T P^T on
 //     v_mfma_f32_32x32x16_bf16 (fp8: v_mfma_f32_32x32x64_f8f6f4), so every
 //     lane owns ONE query column of S^T and of O^T: the softmax row max and sum
@@ -17,11 +14,15 @@
 //   * the S^T accumulator (keys 8i+4h+j of the lane's query) is the P^T
 //     operand of the PV product as it stands: the contraction over keys only
 //     needs V^T to list keys in the same slot order;
-//   * K and V travel HBM -> registers -> LDS with 16-byte range-checked buffer
-//     loads issued one tile ahead of their use, and land in padded
-//     row-major tiles whose operand reads are free of bank conflicts; V^T
-//     operands come from the row-major tile through transposing LDS reads
-//     (ds_read_b64_tr_b16, fp8: ds_read_b64_tr_b8);
+//   * each key block is handled as two halves of 64 keys.  A half (64 K rows and
+//     64 V rows) goes HBM -> LDS with range-checked direct-to-LDS buffer loads (no
+//     staging registers; rows past a sequence end read as zero) into one of two
+//     LDS buffers that alternate, so the next half streams in while the current
+//     one is computed; one wait and one barrier per half;
+//   * LDS rows are unpadded; the 16-byte chunks of each row are permuted by an XOR
+//     of the row index, chosen so the K operand reads (ds_read_b128) and the V^T
+//     operand reads (ds_read_b64_tr_b16, fp8: ds_read_b64_tr_b8) touch every bank
+//     at most once per cycle;
 //   * lists are ascending with the diagonal last: only the last visited block
 //     needs the causal mask;
 //   * fp32 online softmax in exp2 units with a lazy rescale: O and the row sum
