@@ -77,9 +77,11 @@ def discover(q: torch.Tensor, k: torch.Tensor, q_scale=None, k_scale=None, poole
 
 
 def threshold_compact(pooled_q: torch.Tensor, pooled_k: torch.Tensor, alpha: float, n_sink: int, n_local: int,
-                      softmax_scale: Optional[float] = None, idx=None, counts=None):
+                      softmax_scale: Optional[float] = None, idx=None, counts=None, scores=None):
     """Block scores, alpha x row-max threshold with sink/local blocks, ascending
-    lists -> (idx int32 triangular-packed [hq * nb(nb+1)/2], counts int32 [hq, nb])."""
+    lists -> (idx int32 triangular-packed [hq * nb(nb+1)/2], counts int32 [hq, nb]).
+    scores: optional fp64 [hq, nb, nb] tensor that receives the scaled pooled
+    scores s_ij for j <= i (a debug output; entries j > i are left as they are)."""
     hq, nb, d = pooled_q.shape
     hkv = pooled_k.shape[0]
     if softmax_scale is None:
@@ -89,7 +91,7 @@ def threshold_compact(pooled_q: torch.Tensor, pooled_k: torch.Tensor, alpha: flo
     if counts is None:
         counts = torch.empty((hq, nb), dtype=torch.int32, device=pooled_q.device)
     call("fp_threshold_compact", _ptr(pooled_q), _ptr(pooled_k), nb, hq, hkv, d, float(softmax_scale),
-         float(alpha), int(n_sink), int(n_local), _ptr(idx), _ptr(counts), _stream(pooled_q))
+         float(alpha), int(n_sink), int(n_local), _ptr(idx), _ptr(counts), _ptr(scores), _stream(pooled_q))
     return idx, counts
 
 

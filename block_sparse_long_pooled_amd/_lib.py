@@ -36,7 +36,7 @@ _SIGNATURES = {
     "fp_discover": (c_int, [_p, _p, c_int, _p, _p, c_int, c_int, c_int, c_int, c_int,
                             _i64, _i64, _i64, _i64, _p, _p, _p]),
     "fp_threshold_compact": (c_int, [_p, _p, c_int, c_int, c_int, c_int, c_double, c_double, c_int, c_int,
-                                     _p, _p, _p]),
+                                     _p, _p, _p, _p]),
     "fp_sparse_attn": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),
     "fp_dense_attn": (c_int, [_p, _p, _p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,

@@ -219,7 +219,7 @@ int fp_discover_paged(const void* q, const void* k, int dtype, const float* q_sc
 // ------------------------------------------------------- threshold + compact
 static int select_common(const double* pq, const double* pk, const fp::SeqDesc& sd, int hq, int hkv,
                          double softmax_scale, double alpha, int n_sink, int n_local, int32_t* idx, int32_t* counts,
-                         void* stream, uint32_t* mask = nullptr) {
+                         void* stream, uint32_t* mask = nullptr, double* scores = nullptr) {
   if (pq == nullptr || pk == nullptr) return fail(FP_EINVAL, "pooled input is NULL");
   if (mask == nullptr && (idx == nullptr || counts == nullptr)) return fail(FP_EINVAL, "idx/counts is NULL");
   if (!std::isfinite(alpha) || alpha < 0.0) return fail(FP_EINVAL, "alpha must be finite and >= 0 (got %g)", alpha);
@@ -233,6 +233,7 @@ static int select_common(const double* pq, const double* pk, const fp::SeqDesc& 
   a.log_alpha = alpha == 0.0 ? -HUGE_VAL : std::log(alpha);
   a.n_sink = n_sink; a.n_local = n_local; a.idx = idx; a.counts = counts;
   a.mask = mask; a.mask_words = (int)((sd.max_nb + 31) / 32);
+  a.scores = scores;
   return launch_status(fp::launch_select(a, sd, (hipStream_t)stream));
 }
 
@@ -253,13 +254,15 @@ int fp_threshold_mask(const double* pooled_q, const double* pooled_k, int nb, in
 
 int fp_threshold_compact(const double* pooled_q, const double* pooled_k, int nb, int hq, int hkv, int d,
                          double softmax_scale, double alpha, int n_sink, int n_local,
-                         int32_t* idx, int32_t* counts, void* stream) {
+                         int32_t* idx, int32_t* counts, double* scores, void* stream) {
   int r;
   if ((r = check_shape(FP_BF16, hq, hkv, d, fp::kBlock))) return r;
   if (nb < 0 || nb > (1 << 24)) return fail(FP_EINVAL, "nb=%d out of range", nb);
   if (nb == 0) return ok();
+  if (scores != nullptr && ((uintptr_t)scores & 7u)) return fail(FP_EINVAL, "scores not 8-byte aligned");
   fp::SeqDesc sd = single_seq(nb * fp::kBlock);
-  return select_common(pooled_q, pooled_k, sd, hq, hkv, softmax_scale, alpha, n_sink, n_local, idx, counts, stream);
+  return select_common(pooled_q, pooled_k, sd, hq, hkv, softmax_scale, alpha, n_sink, n_local, idx, counts, stream,
+                       nullptr, scores);
 }
 
 int fp_threshold_compact_varlen(const double* pooled_q, const double* pooled_k, const int32_t* cu_seqlens,

@@ -60,6 +60,7 @@ struct SelectLaunch {
   int32_t* counts;            // [hq, total_blocks]
   uint32_t* mask;             // bit-packed keep mask [hq, nb, mask_words] instead of lists, or nullptr
   int mask_words;             // ceil(nb / 32)
+  double* scores;             // single sequence only: scaled pooled scores [hq, nb, nb] (j <= i written), or nullptr
 };
 
 struct AttnLaunch {

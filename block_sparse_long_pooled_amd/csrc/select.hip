@@ -126,7 +126,10 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int j = jt * kTile + 16 * t + lc;
-          if (j <= i && r < nq) rmax[v] = fmax(rmax[v], acc[t][v] * a.scale);
+          if (j <= i && r < nq) {
+            rmax[v] = fmax(rmax[v], acc[t][v] * a.scale);
+            if (a.scores != nullptr) a.scores[((int64_t)h * nq + r) * nk + j] = acc[t][v] * a.scale;
+          }
         }
       }
       if (q == nt - 1) {

@@ -115,6 +115,8 @@ int fp_discover(const void* q, const void* k, int dtype,
  *   idx    out: ascending kept j per (h, i), triangular-packed (see above);
  *          capacity fp_idx_capacity(hq, nb) int32
  *   counts out: [hq, nb] int32 list lengths (>= 1)
+ *   scores optional debug output, NULL to skip: [hq, nb, nb] fp64, 8-byte
+ *          aligned; s_ij is written for j <= i, entries j > i are not touched
  *
  * alpha must be finite and >= 0 (alpha = 0 keeps every causal block, alpha > 1
  * keeps only the forced blocks); n_sink >= 0; n_local >= 1.  softmax_scale
@@ -123,7 +125,7 @@ int fp_discover(const void* q, const void* k, int dtype,
 int fp_threshold_compact(const double* pooled_q, const double* pooled_k,
                          int nb, int hq, int hkv, int d,
                          double softmax_scale, double alpha, int n_sink, int n_local,
-                         int32_t* idx, int32_t* counts, void* stream);
+                         int32_t* idx, int32_t* counts, double* scores, void* stream);
 
 /* ---------------------------------------------------------------------------
  * fp_sparse_attn -- causal GQA block-sparse flash attention (Method 3: the

@@ -69,16 +69,17 @@ def test_discover_rejects(kw, code):
 
 def select(**kw):
     a = dict(pq=P, pk=P, nb=32, hq=4, hkv=2, d=128, scale=1 / math.sqrt(128), alpha=0.1, ns=1, nl=2,
-             idx=P, cnt=P, stream=None)
+             idx=P, cnt=P, scores=None, stream=None)
     a.update(kw)
     return _lib.status_of("fp_threshold_compact", a["pq"], a["pk"], a["nb"], a["hq"], a["hkv"], a["d"],
-                          a["scale"], a["alpha"], a["ns"], a["nl"], a["idx"], a["cnt"], a["stream"])
+                          a["scale"], a["alpha"], a["ns"], a["nl"], a["idx"], a["cnt"], a["scores"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(alpha=-0.1), EINVAL), (dict(alpha=float("nan")), EINVAL), (dict(alpha=float("inf")), EINVAL),
     (dict(nl=0), EINVAL), (dict(ns=-1), EINVAL), (dict(scale=0.0), EINVAL), (dict(idx=None), EINVAL),
     (dict(cnt=None), EINVAL), (dict(d=96), EUNSUP), (dict(hq=5, hkv=2), EINVAL), (dict(nb=-3), EINVAL),
+    (dict(scores=P + 4), EINVAL),
 ])
 def test_threshold_rejects(kw, code):
     assert select(**kw) == code

@@ -95,6 +95,30 @@ def test_lists_and_attention_match_oracle(name):
         assert np.max(np.abs(r["lse"] - ref_lse.astype(np.float32))) <= 1e-3 * max(1.0, np.abs(ref_lse).max())
 
 
+@pytest.mark.parametrize("name", CASES)
+def test_scores_match_oracle(name):
+    """The debug score output: fp64 pooled scores on the fp64 matrix core against the
+    oracle's score map (same pooled means, bit-exact inputs; only the summation order
+    differs), written for j <= i only; lists are the same with and without it."""
+    wl = workload(name)
+    print(f"[case] scores {name}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
+    pq, pk = fp.discover(q, k, qs, ks)
+    hq, nb, _ = pq.shape
+    sc = torch.full((hq, nb, nb), float("nan"), dtype=torch.float64, device=q.device)
+    alpha = wl.alphas[0]
+    idx1, cnt1 = fp.threshold_compact(pq, pk, alpha, wl.n_sink, wl.n_local, scores=sc)
+    idx0, cnt0 = fp.threshold_compact(pq, pk, alpha, wl.n_sink, wl.n_local)
+    torch.cuda.synchronize()
+    ref = O.block_scores(pq.cpu().numpy(), pk.cpu().numpy(), 1.0 / math.sqrt(128))
+    got = sc.cpu().numpy()
+    low = np.tril(np.ones((nb, nb), dtype=bool))
+    assert np.all(np.isnan(got[:, ~low]))
+    diff = np.abs(got[:, low] - ref[:, low])
+    assert np.all(diff <= 1e-12 * np.maximum(1.0, np.abs(ref[:, low])))
+    assert torch.equal(cnt0, cnt1) and torch.equal(idx0, idx1)
+
+
 @pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block"])
 def test_dense_matches_oracle(name):
     wl = workload(name)
