@@ -361,11 +361,14 @@ def device_tensors(wl: Workload, device="cuda"):
 
 
 def device_pages(wl: Workload, device="cuda"):
-    """(k_cache, v_cache, page_table) of a paged bf16 workload as torch tensors."""
+    """(k_cache, v_cache, page_table) of a paged workload as torch tensors (bf16, or
+    uint8 e4m3fn codes whose scales are those of device_tensors)."""
     import torch
 
-    assert wl.paged and wl.dtype == "bf16"
+    assert wl.paged
 
     def conv(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return conv(wl.k_cache), conv(wl.v_cache), torch.from_numpy(wl.page_table).to(device)

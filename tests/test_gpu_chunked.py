@@ -31,7 +31,7 @@ def case(name):
     elif name == "fp8":
         lk = [128 * 12 + 3, 128 * 4]
         lq = [200, 128 * 4]
-        wl = synth.make_workload(name, 8, 2, lk, seed=32, dtype="fp8", n_sink=1, n_local=4)
+        wl = synth.make_workload(name, 8, 2, lk, seed=32, dtype="fp8", paged=True, n_sink=1, n_local=4)
     else:
         raise KeyError(name)
     return wl, lq
@@ -92,7 +92,7 @@ def gpu_lists(res, h, s):
     return out
 
 
-@pytest.mark.parametrize("name,paged", [("bf16_paged", False), ("bf16_paged", True), ("fp8", False)])
+@pytest.mark.parametrize("name,paged", [("bf16_paged", False), ("bf16_paged", True), ("fp8", False), ("fp8", True)])
 def test_chunked_discover_bit_exact(name, paged):
     print(f"[case] chunked discover {name} paged={paged}", flush=True)
     wl, lq, res = run(name, paged)
@@ -105,7 +105,7 @@ def test_chunked_discover_bit_exact(name, paged):
         assert np.array_equal(res["pk"][:, k0:k1], O.pool(k, 128)), s
 
 
-@pytest.mark.parametrize("name,paged", [("bf16_paged", False), ("bf16_paged", True), ("fp8", False)])
+@pytest.mark.parametrize("name,paged", [("bf16_paged", False), ("bf16_paged", True), ("fp8", False), ("fp8", True)])
 def test_chunked_lists_and_attention_match_oracle(name, paged):
     print(f"[case] chunked lists + attention {name} paged={paged}", flush=True)
     wl, lq, res = run(name, paged)
@@ -152,10 +152,11 @@ def test_chunked_dense_matches_oracle():
         assert np.max(np.abs(res["out"][cu_q[s]:cu_q[s + 1]] - ref)) <= TOL_BF16, s
 
 
-def test_chunked_paged_equals_packed_bit_exact():
-    print("[case] chunked paged vs packed", flush=True)
-    _, _, a = run("bf16_paged", paged=False)
-    _, _, b = run("bf16_paged", paged=True)
+@pytest.mark.parametrize("name", ["bf16_paged", "fp8"])
+def test_chunked_paged_equals_packed_bit_exact(name):
+    print(f"[case] chunked paged vs packed {name}", flush=True)
+    _, _, a = run(name, paged=False)
+    _, _, b = run(name, paged=True)
     for key in ("pq", "pk", "idx", "counts", "out", "lse"):
         assert np.array_equal(a[key], b[key], equal_nan=True), key
 

@@ -193,25 +193,28 @@ def test_strided_inputs_match_contiguous():
 
 # ----------------------------------------------------------------- varlen / paged
 @functools.lru_cache(maxsize=None)
-def batch_workload():
+def batch_workload(dtype="bf16"):
     # ragged lengths: partial tails, one single-block sequence, one > 64 blocks
     return synth.make_workload("paged_small", 8, 2, [1000, 128, 65, 8300, 3000], seed=31, paged=True,
-                               alphas=(0.1,), n_sink=1, n_local=4)
+                               dtype=dtype, alphas=(0.1,), n_sink=1, n_local=4)
 
 
-def test_varlen_paged_matches_oracle_and_packed():
-    wl = batch_workload()
-    print(f"[case] paged lengths={wl.lengths}", flush=True)
-    q, k, v, *_ = to_device(wl)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_varlen_paged_matches_oracle_and_packed(dtype):
+    wl = batch_workload(dtype)
+    print(f"[case] paged {dtype} lengths={wl.lengths}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
     kc, vc, table = to_device_paged(wl)
     batch = fp.VarlenBatch(wl.lengths, q.device)
-    pq1, pk1 = fp.discover_paged(q, k, batch)
-    pq2, pk2 = fp.discover_paged(q, kc, batch, page_table=table)
+    pq1, pk1 = fp.discover_paged(q, k, batch, q_scale=qs, k_scale=ks)
+    pq2, pk2 = fp.discover_paged(q, kc, batch, page_table=table, q_scale=qs, k_scale=ks)
     idx, counts = fp.threshold_compact_varlen(pq2, pk2, batch, 0.1, wl.n_sink, wl.n_local)
-    o_packed = fp.sparse_attn_paged(q, k, v, batch, idx, counts)
-    o_paged, lse = fp.sparse_attn_paged(q, kc, vc, batch, idx, counts, page_table=table, return_lse=True)
-    d_paged = fp.sparse_attn_paged(q, kc, vc, batch, page_table=table)
+    sc = dict(q_scale=qs, k_scale=ks, v_scale=vs)
+    o_packed = fp.sparse_attn_paged(q, k, v, batch, idx, counts, **sc)
+    o_paged, lse = fp.sparse_attn_paged(q, kc, vc, batch, idx, counts, page_table=table, return_lse=True, **sc)
+    d_paged = fp.sparse_attn_paged(q, kc, vc, batch, page_table=table, **sc)
     torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_FP8
     assert torch.equal(pq1, pq2) and torch.equal(pk1, pk2)
     assert torch.equal(o_packed, o_paged)
 
@@ -231,9 +234,9 @@ def test_varlen_paged_matches_oracle_and_packed():
         check_lists(lists, sels[s], 0.1, wl.n_sink, wl.n_local)
         a, b = cu[s], cu[s + 1]
         ref = O.sparse_attention(oq[a:b], ok_[a:b], ov[a:b], lists, 128)
-        assert np.max(np.abs(out[a:b] - ref)) <= TOL_BF16, s
+        assert np.max(np.abs(out[a:b] - ref)) <= tol, s
         dref = O.dense_attention(oq[a:b], ok_[a:b], ov[a:b])
-        assert np.max(np.abs(dout[a:b] - dref)) <= TOL_BF16, s
+        assert np.max(np.abs(dout[a:b] - dref)) <= tol, s
 
 
 def test_varlen_single_sequence_equals_contiguous_api():
