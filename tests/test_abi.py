@@ -109,6 +109,16 @@ def test_sparse_attn_rejects(kw, code):
     assert attn(**kw) == code
 
 
+@pytest.mark.parametrize("kw,msg", [
+    (dict(L=2**31 - 1, hq=2048, hkv=2), b"grid too large"),   # hq * nb work items in a 1-D grid
+    (dict(hq=4097, hkv=1), b"too large"),
+    (dict(st=[2**24, 128, 256, 128, 256, 128, 512, 128]), b"32-bit tile offsets"),  # Q stride
+    (dict(st=[512, 128, 2**24, 128, 256, 128, 512, 128]), b"32-bit tile offsets"),  # K stride
+])
+def test_sparse_attn_size_limits(kw, msg):
+    assert attn(**kw) == EINVAL and msg in _lib.load().fp_last_error()
+
+
 def test_dense_attn_rejects():
     assert attn("fp_dense_attn", out=None) == EINVAL
     assert attn("fp_dense_attn", block=256) == EUNSUP
