@@ -347,7 +347,7 @@ def cpu_baseline(wl, alpha, dense_eq_flops, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "single-GPU implementation (no collectives or sharding): --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch  # noqa: F401
