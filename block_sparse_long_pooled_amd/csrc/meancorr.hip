@@ -1,6 +1,6 @@
-// V2 mean correction, as a switchable assumption.  FlashPrefill V2 (abstract)
-// names "a mean correction term that suppresses the approximation error" but does
-// not define it.  Reading implemented here: every causal key block that the list of
+// V2 mean correction, as a switchable assumption.  The FlashPrefill V2 abstract
+// mentions a mean-based correction that reduces the error of the sparse
+// approximation, without a formula.  Reading implemented here: every causal key block that the list of
 // (h, i) prunes still enters the softmax, as n_j = 128 copies of its mean key kbar_j
 // carrying its mean value vbar_j.  The pass runs after the sparse attention and
 // folds the pruned blocks into its result:

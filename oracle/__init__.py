@@ -392,8 +392,9 @@ def select_blocks_grouped(q: np.ndarray, k: np.ndarray, block: int, alpha: float
 # --------------------------------------- V2 mean correction (an assumption)
 def mean_correction(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists, block: int,
                     scale: Optional[float] = None, want_lse: bool = False):
-    """ASSUMPTION, not defined on the pages ([V2] abstract only names a mean correction
-    term that suppresses the approximation error).  Reading: sparse attention over the
+    """ASSUMPTION, not defined on the pages (the [V2] abstract mentions a mean-based
+    correction meant to reduce the sparse approximation's error, with no formula).
+    Reading: sparse attention over the
     lists, plus every causal block j missing from the list of (h, i) entering the
     softmax as n_j copies of its mean key kbar_j with its mean value vbar_j:
 
