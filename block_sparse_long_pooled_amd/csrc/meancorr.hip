@@ -1,9 +1,9 @@
 // V2 mean correction, as a switchable assumption.  The FlashPrefill V2 abstract
 // mentions a mean-based correction that reduces the error of the sparse
-// approximation, without a formula.  Reading implemented here: every causal key block that the list of
-// (h, i) prunes still enters the softmax, as n_j = 128 copies of its mean key kbar_j
-// carrying its mean value vbar_j.  The pass runs after the sparse attention and
-// folds the pruned blocks into its result:
+// approximation, without a formula.  Reading implemented here: every causal key
+// block that the list of (h, i) prunes still enters the softmax, as n_j = 128
+// copies of its mean key kbar_j carrying its mean value vbar_j.  The pass runs
+// after the sparse attention and folds the pruned blocks into its result:
 //
 //   O' = (Z O + sum_j n_j e^{s_j} vbar_j) / (Z + sum_j n_j e^{s_j}),
 //   s_j = scale * q . kbar_j,  Z = e^{LSE},  LSE' = log(Z + sum_j n_j e^{s_j}).
