@@ -429,6 +429,17 @@ def main():
             "attn_computed_tflops": c8 / (r8["attn_ms"] * 1e-3) / 1e12,
             "mfma_frac_fp8": c8 / (r8["attn_ms"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
         }
+        if not args.no_dense:
+            # the same-GPU dense fp8 kernel on the same inputs (dense-equivalent causal
+            # work 2 hq d L^2, as for the bf16 dense figure)
+            dm8 = time_dense(r8["tensors"], reps=1)
+            dense8 = 2.0 * wl8.hq * d * L8 * L8
+            extra["fp8_256k"].update({
+                "dense_attn_ms": dm8,
+                "dense_attn_mfma_frac_fp8": dense8 / (dm8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                "speedup_vs_dense_step": dm8 / r8["ms_per_step"],
+            })
+            log(f"fp8 256K dense attention {dm8:.1f} ms")
         del r8["tensors"], r8["pooled"], r8["lists"], wl8
         log(f"fp8 256K step {extra['fp8_256k']['ms_per_step']:.2f} ms")
 
