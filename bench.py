@@ -171,6 +171,63 @@ def time_chunked(r, wl, alpha, chunk, reps=3):
     }
 
 
+def time_paged_batch(alpha, reps=3):
+    """The continuous-batching workload: 8 ragged sequences (lengths U{4K..64K}) with K/V
+    in 128-token pages under a permuted page table; discover_paged +
+    threshold_compact_varlen + sparse_attn_paged per step (HIP events per stage), and
+    the same step with packed K/V for comparison."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    import synth
+    wl = synth.make_config(4)
+    dev = torch.device("cuda", 0)
+    q, k, v, qs, ks, vs = synth.device_tensors(wl, dev)
+    kc, vc, table = synth.device_pages(wl, dev)
+    batch = fp.VarlenBatch(wl.lengths, dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+
+    def once(paged, ev=None):
+        kk, vv, pt = (kc, vc, table) if paged else (k, v, None)
+        if ev:
+            ev[0].record()
+        pq, pk = fp.discover_paged(q, kk, batch, page_table=pt, q_scale=qs, k_scale=ks)
+        if ev:
+            ev[1].record()
+        idx, counts = fp.threshold_compact_varlen(pq, pk, batch, alpha, wl.n_sink, wl.n_local)
+        if ev:
+            ev[2].record()
+        fp.sparse_attn_paged(q, kk, vv, batch, idx, counts, page_table=pt, q_scale=qs, k_scale=ks, v_scale=vs,
+                             out=out)
+        if ev:
+            ev[3].record()
+        return counts
+
+    res = {"workload": f"{wl.name}: {wl.n_seqs} sequences, {int(sum(wl.lengths))} tokens, "
+                       f"{int(table.shape[0])}x{int(table.shape[1])} page table"}
+    d = q.shape[2]
+    dense_eq = sum(2.0 * wl.hq * d * n * n for n in wl.lengths)
+    for paged in (True, False):
+        counts = once(paged)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for e in evs:
+            once(paged, e)
+        torch.cuda.synchronize()
+        st = np.array([[e[x].elapsed_time(e[x + 1]) for x in range(3)] for e in evs]).mean(axis=0)
+        tiles = int(counts.sum().item())
+        comp = tiles * 4.0 * BLOCK * BLOCK * d / (st[2] * 1e-3) / 1e12
+        res["paged" if paged else "packed"] = {
+            "stage_ms": {"discover": float(st[0]), "threshold_compact": float(st[1]), "sparse_attn": float(st[2])},
+            "ms_per_step": float(st.sum()),
+            "dense_equiv_tflops": dense_eq / (st.sum() * 1e-3) / 1e12,
+            "attn_computed_tflops": comp, "mfma_frac": comp / PEAK_BF16_TFLOPS,
+        }
+    res["density"] = tiles / sum(wl.hq * (-(-n // BLOCK)) * (-(-n // BLOCK) + 1) / 2 for n in wl.lengths)
+    del q, k, v, kc, vc, out
+    return res
+
+
 def time_grouped(r, wl, alpha, reps=2):
     """Group-shared lists on the same inputs: per-head masks, their union per KV
     group, and attention with every head reading its group's list."""
@@ -415,6 +472,11 @@ def main():
 
     if not args.no_extra and args.config == 2:
         import torch
+        torch.cuda.empty_cache()
+        extra["paged_batch"] = time_paged_batch(alpha)
+        pb = extra["paged_batch"]
+        log(f"paged batch step {pb['paged']['ms_per_step']:.2f} ms (packed K/V {pb['packed']['ms_per_step']:.2f} ms), "
+            f"attention {pb['paged']['mfma_frac'] * 100:.1f}% of MFMA peak")
         torch.cuda.empty_cache()
         wl8 = synth.make_config(3)
         r8 = time_hot_path(wl8, max(2, args.steps // 2), 1, wl8.alphas[0])
