@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FLASHPREFILL_LIB") or os.path.join(HERE, "libflashprefill.so")
 
 FP_OK, FP_EINVAL, FP_EUNSUPPORTED, FP_EHIP = 0, 1, 2, 3
+ABI_VERSION = 2  # the signatures below; the library must report the same version
 FP_BF16, FP_FP8_E4M3 = 0, 1
 
 
@@ -87,6 +88,10 @@ def load():
             f"{LIB_PATH} is missing: build it with `python -m block_sparse_long_pooled_amd.build` "
             "(there is no CPU fallback for the HIP path)")
     lib = ctypes.CDLL(LIB_PATH)
+    lib.fp_abi_version.restype = c_int
+    if lib.fp_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.fp_abi_version()}, the binding expects {ABI_VERSION}: "
+                          "rebuild it with `python -m block_sparse_long_pooled_amd.build`")
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

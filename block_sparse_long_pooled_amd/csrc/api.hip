@@ -144,7 +144,7 @@ const char* fp_status_string(int status) {
 
 const char* fp_last_error(void) { return g_last_error.c_str(); }
 
-int fp_abi_version(void) { return 1; }
+int fp_abi_version(void) { return 2; }
 
 int64_t fp_num_blocks(int64_t L, int block) { return block > 0 && L >= 0 ? (L + block - 1) / block : -1; }
 

@@ -77,7 +77,7 @@ enum fp_dtype {
 const char* fp_status_string(int status);
 /* Description of the last error returned on this host thread ("" if none). */
 const char* fp_last_error(void);
-/* Library ABI version (increments on any signature change). */
+/* Library ABI version (increments on any signature change; this header: 2). */
 int fp_abi_version(void);
 
 /* Host helpers: number of blocks ceil(L / block), and the idx capacity in
