@@ -44,7 +44,7 @@ def test_single_sequence_config(k):
     for alpha in wl.alphas:
         pq, pk = fp.discover(q, kk, qs, ks)
         idx, counts = fp.threshold_compact(pq, pk, alpha, wl.n_sink, wl.n_local)
-        out = fp.sparse_attn(q, kk, v, idx, counts, qs, ks, vs)
+        out, lse = fp.sparse_attn(q, kk, v, idx, counts, qs, ks, vs, return_lse=True)
         torch.cuda.synchronize()
         assert np.array_equal(pq.cpu().numpy(), pq_ref)
         assert np.array_equal(pk.cpu().numpy(), pk_ref)
@@ -59,28 +59,36 @@ def test_single_sequence_config(k):
         n_amb = check_lists(lists, dict(P=P, keep=keep), alpha, wl.n_sink, wl.n_local)
         del P, keep
         out_np = out.float().cpu().numpy()
+        lse_np = lse.cpu().numpy()
         worst = 0.0
         for h, i in sample_rows(wl.hq, nb, 8, seed=100 + k):
-            ref = O.attend_block(oq, ok_, ov, lists[h][i], h, i, 128)
+            ref, ref_lse = O.attend_block(oq, ok_, ov, lists[h][i], h, i, 128, want_lse=True)
             err = float(np.max(np.abs(out_np[i * 128:(i + 1) * 128, h] - ref)))
             worst = max(worst, err)
             assert err <= tol, (h, i, err)
+            # same LSE rule as the small-size parity tests
+            lerr = float(np.max(np.abs(lse_np[h, i * 128:(i + 1) * 128] - ref_lse)))
+            assert lerr <= 1e-3 * max(1.0, float(np.abs(ref_lse).max())), (h, i, lerr)
         print(f"  alpha={alpha}: density {cnt_np.sum() / (wl.hq * tri):.4f}, in-band {n_amb}, "
               f"sampled max-abs {worst:.3e}", flush=True)
 
 
-def test_dense_sampled_rows_128k():
-    wl = cfg(2)
-    print("[case] dense 128K sampled rows", flush=True)
-    q, kk, v, *_ = to_device(wl)
-    out = fp.dense_attn(q, kk, v)
+@pytest.mark.parametrize("k", [2, 3])
+def test_dense_sampled_rows(k):
+    """The same-GPU dense kernel at 128K bf16 and 256K fp8, sampled query blocks."""
+    wl = cfg(k)
+    print(f"[case] dense {wl.name} sampled rows", flush=True)
+    q, kk, v, qs, ks, vs = to_device(wl)
+    out = fp.dense_attn(q, kk, v, qs, ks, vs)
     torch.cuda.synchronize()
     oq, ok_, ov = oracle_inputs(wl)
     out_np = out.float().cpu().numpy()
-    nb = 1024
+    del out
+    nb = -(-wl.L // 128)
+    tol = TOL_BF16 if wl.dtype == "bf16" else TOL_FP8
     for h, i in sample_rows(wl.hq, nb, 4, seed=7):
         ref = O.attend_block(oq, ok_, ov, np.arange(i + 1), h, i, 128)
-        assert np.max(np.abs(out_np[i * 128:(i + 1) * 128, h] - ref)) <= TOL_BF16
+        assert np.max(np.abs(out_np[i * 128:(i + 1) * 128, h] - ref)) <= tol, (h, i)
 
 
 def test_paged_batch_config():
