@@ -9,6 +9,7 @@ import torch
 import block_sparse_long_pooled_amd as fp
 import oracle as O
 from helpers import TOL_BF16, TOL_FP8, oracle_inputs, to_device, unpack_lists
+import synth
 from test_gpu_parity import workload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -57,3 +58,29 @@ def test_mean_correction_is_noop_without_pruning():
     fp.mean_correct(q, pk, pv, idx, counts, o2, l2, q_scale=qs)
     torch.cuda.synchronize()
     assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("L", [100, 129, 128 * 33 + 5])
+def test_mean_correction_edge_lengths(L):
+    """One partial block (nothing below the diagonal), two blocks, and a ragged
+    33-block sequence with alpha > 1, no sink and a 1-block window, so every
+    off-diagonal block is pruned and enters through its mean."""
+    wl = synth.make_workload(f"mc_edge_{L}", 4, 2, [L], seed=41, alphas=(1.5,), n_sink=0, n_local=1)
+    print(f"[case] mean correction edge L={L}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
+    pq, pk = fp.discover(q, k, qs, ks)
+    pv = fp.pool(v, vs)
+    idx, counts = fp.threshold_compact(pq, pk, 1.5, 0, 1)
+    out, lse = fp.sparse_attn(q, k, v, idx, counts, qs, ks, vs, return_lse=True)
+    o0, l0 = out.clone(), lse.clone()
+    fp.mean_correct(q, pk, pv, idx, counts, out, lse, q_scale=qs)
+    torch.cuda.synchronize()
+    nb = -(-L // 128)
+    assert torch.equal(counts.cpu(), torch.ones((wl.hq, nb), dtype=torch.int32))
+    lists = [unpack_lists(idx.cpu().numpy(), counts.cpu().numpy(), h, nb, nb * (nb + 1) // 2) for h in range(wl.hq)]
+    oq, ok_, ov = oracle_inputs(wl)
+    ref, ref_lse = O.mean_correction(oq, ok_, ov, lists, 128, want_lse=True)
+    assert np.max(np.abs(out.float().cpu().numpy() - ref)) <= TOL_BF16
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-3 * max(1.0, np.abs(ref_lse).max())
+    # block 0 has nothing to correct: its rows are untouched
+    assert torch.equal(out[:min(L, 128)], o0[:min(L, 128)]) and torch.equal(lse[:, :min(L, 128)], l0[:, :min(L, 128)])
