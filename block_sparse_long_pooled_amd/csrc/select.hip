@@ -30,7 +30,7 @@ struct SelK {
 };
 
 template <bool MASK>
-__global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
+__global__ __launch_bounds__(kThreads, 2) void select_kernel(SelK p) {
   const SelectLaunch& a = p.a;
   const int it = gridDim.x - 1 - blockIdx.x;  // row tiles with the longest rows first
   const int s = blockIdx.y;
@@ -49,10 +49,10 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
   const double* Qb = a.pq + ((int64_t)h * p.sd.total_qblocks + sp.qblk0) * kHeadDim;
   const double* Kb = a.pk + ((int64_t)g * p.sd.total_blocks + sp.blk0) * kHeadDim;
 
-  // The query tile stays in LDS for both passes; key tiles stream through LDS and
-  // the next one is in registers while the current one is used.  d-major layout:
-  // a thread reads 4 consecutive rows (or columns) of one d as two 16-byte reads.
-  __shared__ __attribute__((aligned(16))) double Qs[kHeadDim][kTile];
+  // Key tiles stream through LDS (d-major, [d][column]) and the next one is in
+  // registers while the current one is used.  The query tile passes through the
+  // same LDS buffer once, at the start, into each lane's A operands, which then stay
+  // in registers for both passes; with 64 KB of LDS two workgroups share a CU.
   __shared__ __attribute__((aligned(16))) double Ks[kHeadDim][kTile];
 
   const int tid = threadIdx.x;
@@ -89,20 +89,23 @@ __global__ __launch_bounds__(kThreads, 1) void select_kernel(SelK p) {
   // group: lane lc of group lg holds rows 16w + lg + 4v (v = 0..3) at columns
   // 16t + lc (t = 0..3) in acc[t][v].
   f64x4 acc[4];
+  double qa[kHeadDim / 4];  // A operand of step ks: row 16w + lc, d = 4ks + lg
   auto tile_scores = [&]() {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
+#pragma unroll
     for (int ks = 0; ks < kHeadDim / 4; ++ks) {
-      const double av = Qs[4 * ks + lg][16 * w + lc];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Ks[4 * ks + lg][16 * t + lc], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], Ks[4 * ks + lg][16 * t + lc], acc[t], 0, 0, 0);
     }
   };
 
   load_rows(Qb, row0, nq);
-  store_rows(Qs);
+  store_rows(Ks);
+  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < kHeadDim / 4; ++ks) qa[ks] = Ks[4 * ks + lg][16 * w + lc];
   load_rows(Kb, 0, nk);
 
   double rmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
