@@ -21,7 +21,9 @@
  *   - Every tensor argument is a DEVICE pointer owned by the caller.  Nothing
  *     is allocated, freed or synchronised inside the library; each call only
  *     enqueues kernels on `stream` (a hipStream_t passed as void*, NULL = the
- *     default stream) and returns.  There is no global mutable state apart
+ *     default stream) and returns, so a sequence of calls on caller-owned
+ *     buffers can be captured into a HIP graph and replayed.  There is no
+ *     global mutable state apart
  *     from a thread-local error message, so calls from several host threads
  *     are safe.
  *   - Head dimension d and block size B must both be 128.  hq % hkv == 0;
