@@ -23,9 +23,8 @@
  *     enqueues kernels on `stream` (a hipStream_t passed as void*, NULL = the
  *     default stream) and returns, so a sequence of calls on caller-owned
  *     buffers can be captured into a HIP graph and replayed.  There is no
- *     global mutable state apart
- *     from a thread-local error message, so calls from several host threads
- *     are safe.
+ *     global mutable state apart from a thread-local error message, so calls
+ *     from several host threads are safe.
  *   - Head dimension d and block size B must both be 128.  hq % hkv == 0;
  *     query head h reads KV head h / (hq / hkv).
  *   - Strides are in ELEMENTS; the innermost (head-dim) stride is 1.  Data
