@@ -75,7 +75,9 @@ __device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const unsigned ch
 }
 
 // Modes (separate instances, so each workload has its own kernel):
-//   kPrefill  per-head lists, queries = keys of each sequence;
+//   kPrefill  per-head lists, one sequence, queries = keys;
+//   kVarlen   the same over a packed batch of sequences (cu_seqlens), K/V packed
+//             or paged;
 //   kMasked   the logical-skip ablation (FlashPrefill Method 3 contrasts it with
 //             physical jumps): the loop visits every causal block j <= i, tests
 //             bit j of the row's block mask and branches past unselected blocks.
@@ -84,7 +86,7 @@ __device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const unsigned ch
 //   kGrouped  one list per KV group, read by every query head of the group;
 //   kChunked  chunked / prefix-cached prefill: queries are the last positions of
 //             each sequence, query blocks follow absolute positions.
-enum { kPrefill = 0, kMasked = 1, kGrouped = 2, kChunked = 3 };
+enum { kPrefill = 0, kMasked = 1, kGrouped = 2, kChunked = 3, kVarlen = 4 };
 
 template <int DT, bool PAGED, bool DENSE, bool LSE, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
@@ -526,9 +528,11 @@ void launch_dt(const AttnK& p, const PageDesc& pd, dim3 grid, hipStream_t st) {
   else if (p.sd.cu_seqlens_q != nullptr) {
     if (paged) launch_t<DT, true, kChunked>(p, grid, st);
     else launch_t<DT, false, kChunked>(p, grid, st);
+  } else if (p.sd.cu_seqlens != nullptr) {
+    if (paged) launch_t<DT, true, kVarlen>(p, grid, st);
+    else launch_t<DT, false, kVarlen>(p, grid, st);
   } else {
-    if (paged) launch_t<DT, true, kPrefill>(p, grid, st);
-    else launch_t<DT, false, kPrefill>(p, grid, st);
+    launch_t<DT, false, kPrefill>(p, grid, st);
   }
 }
 
