@@ -6,7 +6,9 @@ alpha = 0 and alpha > 1, single-key rows, equal keys), a hand-worked example, br
 force with pure-Python loops on tiny inputs, and invariants (forced blocks,
 monotone in alpha, GQA == MHA with repeated K/V).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -89,25 +91,27 @@ def test_pool_partial_block_divides_by_valid_rows():
 
 
 # ----------------------------------------------------------- hand-worked example
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    """A fixture under tests/golden/: '#' comment lines, then a JSON body."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.loads("".join(line for line in f if not line.lstrip().startswith("#")))
+
+
 def test_hand_worked_selection():
-    """Three 2-token blocks, d = 2, by hand:
-    qbar = (1,0), (0,2), (1,1); kbar = (1,0), (0,1), (0,0).
-    Row 1 logits (x sqrt 2): [0, 2] -> P = [e^-sqrt2, 1] = [0.2431, 1].
-    Row 2 logits (x sqrt 2): [1, 1, 0] -> P = [1, 1, e^-(1/sqrt2)] = [1, 1, 0.4931]."""
-    q = np.array([[1, 0], [1, 0], [0, 2], [0, 2], [1, 1], [1, 1]], float)[:, None, :]
-    k = np.array([[2, 0], [0, 0], [0, 1], [0, 1], [1, 1], [-1, -1]], float)[:, None, :]
-    r = O.select_blocks(q, k, 2, alpha=0.25, n_sink=0, n_local=1)
-    assert r["P"][0, 1, 0] == pytest.approx(math.exp(-math.sqrt(2)), rel=1e-14)
-    assert r["P"][0, 2, 2] == pytest.approx(math.exp(-1 / math.sqrt(2)), rel=1e-14)
-    assert [list(x) for x in r["lists"][0]] == [[0], [1], [0, 1, 2]]
-    r = O.select_blocks(q, k, 2, alpha=0.24, n_sink=0, n_local=1)
-    assert [list(x) for x in r["lists"][0]] == [[0], [0, 1], [0, 1, 2]]
-    r = O.select_blocks(q, k, 2, alpha=0.5, n_sink=0, n_local=1)
-    assert [list(x) for x in r["lists"][0]] == [[0], [1], [0, 1, 2]]
-    r = O.select_blocks(q, k, 2, alpha=0.9, n_sink=1, n_local=1)
-    assert [list(x) for x in r["lists"][0]] == [[0], [0, 1], [0, 1, 2]]
-    r = O.select_blocks(q, k, 2, alpha=1.01, n_sink=0, n_local=1)
-    assert [list(x) for x in r["lists"][0]] == [[0], [1], [2]]
+    """Three 2-token blocks, d = 2, worked out by hand (tests/golden/hand_worked_selection.txt):
+    the reweighted scores in closed form and the lists of five (alpha, sink, local) settings."""
+    g = _golden("hand_worked_selection.txt")
+    q = np.array(g["q"], float)[:, None, :]
+    k = np.array(g["k"], float)[:, None, :]
+    closed = {"1": 1.0, "exp(-sqrt(2))": math.exp(-math.sqrt(2)), "exp(-1/sqrt(2))": math.exp(-1 / math.sqrt(2))}
+    for c in g["cases"]:
+        r = O.select_blocks(q, k, g["block"], alpha=c["alpha"], n_sink=c["n_sink"], n_local=c["n_local"])
+        for i, j, form in g["P"]:
+            assert r["P"][0, i, j] == pytest.approx(closed[form], rel=1e-14)
+        assert [list(x) for x in r["lists"][0]] == c["lists"], c
 
 
 # ---------------------------------------------------------------- brute force
