@@ -57,6 +57,16 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+    # a stand-alone C++ consumer of the C ABI (run by the GPU tests)
+    capi_src = os.path.join(ROOT, "tests", "capi", "capi_check.cpp")
+    if os.path.exists(capi_src):
+        capi_bin = os.path.join(ROOT, "tests", "capi", "capi_check")
+        _run([HIPCC, f"--offload-arch={ARCH}", "-O2", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}",
+              capi_src, "-o", capi_bin + ".tmp", f"-L{HERE}", "-lflashprefill", f"-Wl,-rpath,{HERE}",
+              "-Wl,-rpath,$ORIGIN/../../block_sparse_long_pooled_amd"])
+        os.replace(capi_bin + ".tmp", capi_bin)
+        if verbose:
+            print(f"built {capi_bin}")
     return LIB_PATH
 
 
