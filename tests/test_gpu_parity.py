@@ -158,6 +158,22 @@ def test_alpha_above_one_keeps_forced_blocks_only():
             assert lst.tolist() == want
 
 
+def test_huge_sink_and_window_keep_everything():
+    """n_sink and n_local far beyond the sequence (no overflow in i - n_local): every
+    causal block is forced, so the sparse output equals the dense kernel bit for bit."""
+    wl = workload("gqa_ragged")
+    q, k, v, *_ = to_device(wl)
+    pq, pk = fp.discover(q, k)
+    nb = pq.shape[1]
+    for ns, nl in [(10 ** 6, 1), (0, 2 ** 31 - 1)]:
+        idx, counts = fp.threshold_compact(pq, pk, 1.5, ns, nl)
+        sp = fp.sparse_attn(q, k, v, idx, counts)
+        de = fp.dense_attn(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(counts.cpu(), torch.arange(1, nb + 1, dtype=torch.int32).repeat(wl.hq, 1)), (ns, nl)
+        assert torch.equal(sp, de), (ns, nl)
+
+
 def test_rerun_is_bit_identical():
     wl = workload("gqa_ragged")
     a = run_gpu(wl, 0.1)
