@@ -120,7 +120,8 @@ def time_hot_path(wl, steps, warmup, alpha):
     stage = np.array([[e[x].elapsed_time(e[x + 1]) for x in range(3)] for e in evs])
     res = dict(ms_per_step=total_ms, wall_s=wall, disc_ms=float(stage[:, 0].mean()),
                thr_ms=float(stage[:, 1].mean()), attn_ms=float(stage[:, 2].mean()),
-               attn_ms_min=float(stage[:, 2].min()), sum_counts=int(counts.sum().item()), nb=nb)
+               attn_ms_min=float(stage[:, 2].min()), sum_counts=int(counts.sum().item()), nb=nb,
+               stage_median=[float(x) for x in np.median(stage, axis=0)])
     res["counts"] = counts
     res["tensors"] = (q, k, v, qs, ks, vs, out)
     res["pooled"] = (pq, pk)
@@ -169,6 +170,28 @@ def time_chunked(r, wl, alpha, chunk, reps=3):
         "listed_tiles": tiles,
         "attn_computed_tflops": tiles * 4.0 * BLOCK * BLOCK * q.shape[2] / (st[2] * 1e-3) / 1e12,
     }
+
+
+def time_discover_cold(r, reps=5):
+    """Discovery with the 256 MB Infinity Cache flushed first (a 512 MB write before
+    each timed call, outside the timed events): the median of `reps` calls."""
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    q, k, v, qs, ks, vs, _ = r["tensors"]
+    pq, pk = r["pooled"]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    ts = []
+    for i in range(reps):
+        flush.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fp.discover(q, k, qs, ks, pooled_q=pq, pooled_k=pk)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del flush
+    return float(np.median(ts))
 
 
 def time_paged_batch(alpha, reps=3):
@@ -439,7 +462,13 @@ def main():
         "discover_gbs": disc_gbs,
         "discover_hbm_frac": disc_gbs / PEAK_HBM_GBS,
         "selection_overhead_frac": (r["disc_ms"] + r["thr_ms"]) / r["ms_per_step"],
+        "stage_ms_median": dict(zip(("discover", "threshold_compact", "sparse_attn"), r["stage_median"])),
     }
+    dcold = time_discover_cold(r)
+    extra["discover_cold_cache"] = {"ms": dcold, "gbs": disc_bytes / (dcold * 1e-3) / 1e9,
+                                    "hbm_frac": disc_bytes / (dcold * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                    "note": "512 MB written before each call to flush the 256 MB Infinity Cache"}
+    log(f"discover with a flushed Infinity Cache {dcold:.3f} ms ({extra['discover_cold_cache']['gbs']:.0f} GB/s)")
     if not args.no_dense:
         dms = time_dense(r["tensors"])
         extra["dense_attn_ms"] = dms
