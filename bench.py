@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload index (2 = 128K bf16)")
+    ap.add_argument("--config", type=int, default=2, choices=(0, 1, 2, 3),
+                    help="single-sequence workload: 0 tiny, 1 32K, 2 128K bf16 (default), 3 256K fp8; the paged "
+                         "8-sequence batch is measured in extra.paged_batch of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the same-GPU dense comparison")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp8 256K side measurement")
