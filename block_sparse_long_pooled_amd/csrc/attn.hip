@@ -23,8 +23,8 @@
 //     of the row index, chosen so the K operand reads (ds_read_b128) and the V^T
 //     operand reads (ds_read_b64_tr_b16, fp8: ds_read_b64_tr_b8) touch every bank
 //     at most once per cycle;
-//   * lists are ascending with the diagonal last: only the last visited block
-//     needs the causal mask;
+//   * lists are ascending with the diagonal last: only block i itself needs the
+//     causal mask, and a list that does not end with i gives NaN rows;
 //   * fp32 online softmax in exp2 units with a lazy rescale: O and the row sum
 //     are rescaled only when the running maximum grows by more than TAU, so P
 //     stays <= 2^TAU; the row sum adds the ROUNDED probabilities, i.e. exactly
@@ -464,7 +464,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
     int jn = entry(min(1, cnt - 1));
     load_half(jc, 0, bufA);
     for (int n = 0; n < cnt; ++n) {
-      const bool diag = n + 1 == cnt;  // only the last entry is the diagonal block
+      // the causal mask belongs to block i itself; a list must end with it, so a
+      // last entry other than i makes the row NaN instead of mis-masking it
+      const bool diag = jc == i;
+      if (n + 1 == cnt && !diag) bad = true;
       __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
       wg_barrier();
       load_half(jc, 1, bufB);

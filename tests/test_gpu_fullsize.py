@@ -1,10 +1,13 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times.
 
 Pooled means are compared bit-exactly everywhere and lists on every row (the
-oracle's pooled score map is cheap).  Attention is checked on sampled query
-blocks the oracle computes one by one (first, last, and seeded random rows of
-random heads), over the GPU's own lists.  Paged == packed is checked bit-exactly
-on the full output of the paged batch.
+oracle's pooled score map is cheap).  Attention is checked on a stratified sample
+of query blocks the oracle computes one by one, over the GPU's own lists: for every
+head its first 4 and last 4 query blocks, plus the 8 rows (past the first four) with
+the fewest listed blocks, where rounding of the probabilities weighs most, and a few
+seeded random rows.  Each test prints its worst max-abs and LSE error against the
+bound.  Paged == packed is checked bit-exactly on the full output of the paged batch,
+and its sample takes every sequence's first and last query block for every head.
 """
 import functools
 
@@ -31,6 +34,39 @@ def sample_rows(hq, nb, n, seed):
     while len(rows) < n:
         rows.add((int(rng.integers(hq)), int(rng.integers(nb))))
     return sorted(rows)
+
+
+def stratified_rows(counts, seed, n_random=8):
+    """Every head's first 4 and last 4 query blocks, the 8 sparsest rows past the
+    first four blocks, and n_random seeded random rows."""
+    hq, nb = counts.shape
+    rows = set()
+    for h in range(hq):
+        for i in list(range(min(4, nb))) + list(range(max(0, nb - 4), nb)):
+            rows.add((h, i))
+    if nb > 4:
+        order = np.argsort(counts[:, 4:], axis=None, kind="stable")[:8]
+        for f in order:
+            rows.add((int(f // (nb - 4)), int(f % (nb - 4)) + 4))
+    rows.update(sample_rows(hq, nb, n_random, seed))
+    return sorted(rows)
+
+
+def check_rows(oq, ok_, ov, lists, out_np, lse_np, rows, tol, label):
+    """Attention and LSE of the given (head, query block) rows against the oracle over
+    the same lists; returns (worst max-abs, worst LSE error)."""
+    worst = worst_lse = 0.0
+    for h, i in rows:
+        ref, ref_lse = O.attend_block(oq, ok_, ov, lists[h][i], h, i, 128, want_lse=True)
+        got = out_np[i * 128:i * 128 + ref.shape[0], h]
+        err = float(np.max(np.abs(got - ref)))
+        worst = max(worst, err)
+        assert err <= tol, f"{label}: row ({h}, {i}) max-abs {err:.3e} > {tol}"
+        if lse_np is not None:
+            lerr = float(np.max(np.abs(lse_np[h, i * 128:i * 128 + ref.shape[0]] - ref_lse)))
+            worst_lse = max(worst_lse, lerr)
+            assert lerr <= 1e-3 * max(1.0, float(np.abs(ref_lse).max())), f"{label}: row ({h}, {i}) LSE {lerr:.3e}"
+    return worst, worst_lse
 
 
 @pytest.mark.parametrize("k", [1, 2, 3])
@@ -60,17 +96,10 @@ def test_single_sequence_config(k):
         del P, keep
         out_np = out.float().cpu().numpy()
         lse_np = lse.cpu().numpy()
-        worst = 0.0
-        for h, i in sample_rows(wl.hq, nb, 8, seed=100 + k):
-            ref, ref_lse = O.attend_block(oq, ok_, ov, lists[h][i], h, i, 128, want_lse=True)
-            err = float(np.max(np.abs(out_np[i * 128:(i + 1) * 128, h] - ref)))
-            worst = max(worst, err)
-            assert err <= tol, (h, i, err)
-            # same LSE rule as the small-size parity tests
-            lerr = float(np.max(np.abs(lse_np[h, i * 128:(i + 1) * 128] - ref_lse)))
-            assert lerr <= 1e-3 * max(1.0, float(np.abs(ref_lse).max())), (h, i, lerr)
+        rows = stratified_rows(cnt_np, seed=100 + k)
+        worst, worst_lse = check_rows(oq, ok_, ov, lists, out_np, lse_np, rows, tol, f"{wl.name} alpha={alpha}")
         print(f"  alpha={alpha}: density {cnt_np.sum() / (wl.hq * tri):.4f}, in-band {n_amb}, "
-              f"sampled max-abs {worst:.3e}", flush=True)
+              f"{len(rows)} sampled rows: max-abs {worst:.3e} (bound {tol}), LSE {worst_lse:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("k", [2, 3])
@@ -86,9 +115,10 @@ def test_dense_sampled_rows(k):
     del out
     nb = -(-wl.L // 128)
     tol = TOL_BF16 if wl.dtype == "bf16" else TOL_FP8
-    for h, i in sample_rows(wl.hq, nb, 4, seed=7):
-        ref = O.attend_block(oq, ok_, ov, np.arange(i + 1), h, i, 128)
-        assert np.max(np.abs(out_np[i * 128:(i + 1) * 128, h] - ref)) <= tol, (h, i)
+    full = [np.arange(i + 1) for i in range(nb)]
+    rows = sorted({(h, i) for h in range(wl.hq) for i in (0, 1, nb - 1)} | set(sample_rows(wl.hq, nb, 4, seed=7)))
+    worst, _ = check_rows(oq, ok_, ov, [full] * wl.hq, out_np, None, rows, tol, f"dense {wl.name}")
+    print(f"  dense {wl.name}: {len(rows)} sampled rows, max-abs {worst:.3e} (bound {tol})", flush=True)
 
 
 def test_paged_batch_config():
@@ -108,6 +138,7 @@ def test_paged_batch_config():
     idx_np, cnt_np = idx.cpu().numpy(), counts.cpu().numpy()
     out_np = o_paged.float().cpu().numpy()
     cu = wl.cu_seqlens
+    worst = 0.0
     for s in range(wl.n_seqs):
         a, b = cu[s], cu[s + 1]
         b0, b1 = batch.cu_blocks[s], batch.cu_blocks[s + 1]
@@ -117,7 +148,9 @@ def test_paged_batch_config():
         nb = b1 - b0
         lists = [unpack_lists(idx_np, cnt_np, h, nb, batch.total_tri, batch.cu_tri[s], b0) for h in range(wl.hq)]
         check_lists(lists, sel, 0.1, wl.n_sink, wl.n_local)
-        for h, i in sample_rows(wl.hq, nb, 3, seed=200 + s):
-            ref = O.attend_block(oq[a:b], ok_[a:b], ov[a:b], lists[h][i], h, i, 128)
-            got = out_np[a + i * 128:a + min((i + 1) * 128, b - a), h]
-            assert np.max(np.abs(got - ref)) <= TOL_BF16, (s, h, i)
+        rows = [(h, i) for h in range(wl.hq) for i in sorted({0, nb - 1})]
+        err, _ = check_rows(oq[a:b], ok_[a:b], ov[a:b], lists, out_np[a:b], None, rows, TOL_BF16,
+                            f"paged batch sequence {s}")
+        worst = max(worst, err)
+    print(f"  paged batch: {wl.n_seqs} sequences x {wl.hq} heads x first/last block, max-abs {worst:.3e} "
+          f"(bound {TOL_BF16})", flush=True)

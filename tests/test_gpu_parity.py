@@ -311,3 +311,25 @@ def test_empty_and_zero_length_sequences():
     e = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=q.device)
     pq0, pk0 = fp.discover(e, e[:, :2])
     assert pq0.shape == (8, 0, 128)
+
+
+def test_list_without_diagonal_gives_nan_rows():
+    """A caller list that does not end with the diagonal block is rejected in the
+    kernel: that (head, query block) comes out NaN, every other row is unchanged."""
+    wl = workload("gqa_ragged")
+    print("[case] list without its diagonal block", flush=True)
+    q, k, v, *_ = to_device(wl)
+    pq, pk = fp.discover(q, k)
+    idx, counts = fp.threshold_compact(pq, pk, 0.1, wl.n_sink, wl.n_local)
+    good = fp.sparse_attn(q, k, v, idx, counts)
+    h, i = 3, 40
+    cut = counts.clone()
+    cut[h, i] -= 1  # drops the last entry, which is block i
+    out = fp.sparse_attn(q, k, v, idx, cut)
+    torch.cuda.synchronize()
+    assert int(counts[h, i]) >= 2
+    rows = slice(i * 128, (i + 1) * 128)
+    assert torch.isnan(out[rows, h].float()).all()
+    keep = torch.ones(out.shape[:2], dtype=torch.bool, device=out.device)
+    keep[rows, h] = False
+    assert torch.equal(out[keep], good[keep])

@@ -44,6 +44,78 @@ def test_decode_e4m3fn_matches_torch():
     assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
 
 
+def _torch_dequant(codes, scales):
+    """Reference for code * scale[head]: torch's own e4m3fn decoder, one head at a time."""
+    out = np.empty(codes.shape, dtype=np.float64)
+    for h in range(codes.shape[1]):
+        vals = torch.from_numpy(np.ascontiguousarray(codes[:, h])).view(torch.float8_e4m3fn).to(torch.float64)
+        out[:, h] = (vals * float(np.float32(scales[h]))).numpy()
+    return out
+
+
+def test_dequantize_every_code_with_per_head_scales():
+    """FP8 inputs (FlashPrefill V2 abstract, FP8 inference): the oracle consumes
+    code * scale[head].  Every code 0..255 (zeros, subnormals, +-448, NaN) under three
+    distinct fp32 scales, each head seeing the codes in its own order, against torch's
+    float8_e4m3fn decoder times the head's scale.  A broadcast on the wrong axis or a
+    division by the scale fails here."""
+    rng = np.random.default_rng(11)
+    scales = np.array([0.5, 3.25, 0.0123], dtype=np.float32)
+    codes = np.empty((256, 3, 4), dtype=np.uint8)
+    for h in range(3):
+        for e in range(4):
+            codes[:, h, e] = rng.permutation(256).astype(np.uint8)
+    ours = O.dequantize(codes, scales)
+    ref = _torch_dequant(codes, scales)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    one = codes == 0x38  # e4m3fn 1.0
+    for h in range(3):
+        assert np.all(ours[:, h][one[:, h]] == np.float64(scales[h]))
+        assert np.max(np.abs(ours[:, h][fin[:, h]])) == 448.0 * np.float64(scales[h])
+
+
+def test_dequantize_gqa_indexes_kv_scales_by_kv_head():
+    """A GQA fp8 workload (4 query heads, 2 KV heads) with per-head scales that all
+    differ: Q dequantises with its 4 scales, K and V with the 2 KV-head scales, each
+    element equal to torch's decoding times the scale of its own head."""
+    wl = synth.make_workload("t8", 4, 2, [300], seed=21, d=32, block=64, dtype="fp8")
+    assert len(set(np.asarray(wl.q_scale).tolist())) == 4 and len(set(np.asarray(wl.k_scale).tolist())) == 2
+    for codes, sc, H in ((wl.q, wl.q_scale, 4), (wl.k, wl.k_scale, 2), (wl.v, wl.v_scale, 2)):
+        assert codes.shape[1] == H and np.asarray(sc).shape == (H,)
+        assert np.array_equal(O.dequantize(codes, sc), _torch_dequant(codes, sc))
+
+
+def test_fp8_workload_end_to_end_matches_sdpa():
+    """FP8 end to end on the oracle side: selection from O.dequantize'd inputs equals the
+    brute-force selection from torch-decoded values, and sparse attention over those
+    lists equals fp64 SDPA (explicit block mask) on the torch-decoded values."""
+    B = 64
+    wl = synth.make_workload("t8e", 4, 2, [450], seed=23, d=32, block=B, dtype="fp8")
+    q, k, v = (O.dequantize(wl.q, wl.q_scale), O.dequantize(wl.k, wl.k_scale),
+               O.dequantize(wl.v, wl.v_scale))
+    tq, tk, tv = (_torch_dequant(wl.q, wl.q_scale), _torch_dequant(wl.k, wl.k_scale),
+                  _torch_dequant(wl.v, wl.v_scale))
+    r = O.select_blocks(q, k, B, 0.2, 1, 2)
+    bf = _brute_force_lists(tq, tk, B, 0.2, 1, 2)
+    for h in range(wl.hq):
+        for i, lst in enumerate(r["lists"][h]):
+            assert list(lst) == bf[h][i]
+    ours = O.sparse_attention(q, k, v, r["lists"], B)
+    L = q.shape[0]
+    g = wl.hq // wl.hkv
+    for h in range(wl.hq):
+        mask = np.zeros((L, L), dtype=bool)
+        for t in range(L):
+            allowed = set(int(x) for x in r["lists"][h][t // B])
+            for c in range(t + 1):
+                mask[t, c] = (c // B) in allowed
+        ref = _sdpa(tq[:, h:h + 1], tk[:, h // g:h // g + 1], tv[:, h // g:h // g + 1], mask=mask[None])
+        assert np.max(np.abs(ours[:, h] - ref[:, 0])) <= 1e-12
+    assert r["counts"].sum() < wl.hq * (r["counts"].shape[1] * (r["counts"].shape[1] + 1)) // 2
+
+
 def test_quantiser_codes_roundtrip_and_saturate():
     """Generator fp8 codes: per-head max |code| is 448 and code*scale is within half an
     e4m3 ulp of the source value (checked through torch's own decoder)."""
