@@ -29,7 +29,9 @@
 //     are rescaled only when the running maximum grows by more than TAU, so P
 //     stays <= 2^TAU; the row sum adds the ROUNDED probabilities, i.e. exactly
 //     the weights that enter P V, so output rows are true convex combinations;
-//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift).
+//   * fp8: e4m3 Q K^T and P V (P rounded to e4m3 after a 2^4 range shift); the
+//     row sum of the rounded P is one more matrix-core product (all-ones operand)
+//     instead of VALU decodes and adds, and three workgroups share a CU.
 #include "fp_device.h"
 
 namespace fp {
@@ -88,8 +90,11 @@ __device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const unsigned ch
 //             each sequence, query blocks follow absolute positions.
 enum { kPrefill = 0, kMasked = 1, kGrouped = 2, kChunked = 3, kVarlen = 4 };
 
+// bf16: two workgroups per CU (<= 256 VGPRs); fp8: three (<= 168 VGPRs), which the
+// fp8 loop needs to keep its matrix cores fed -- except with the LSE output, whose
+// second (unrounded) row sum would not fit without spilling.
 template <int DT, bool PAGED, bool DENSE, bool LSE, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
+__global__ __launch_bounds__(kThreads, (DT == 0 || LSE) ? 2 : 3) void attn_kernel(AttnK p) {
   constexpr bool MASKED = MODE == kMasked;
   constexpr int ES = DT == 0 ? 2 : 1;             // element size in bytes
   constexpr int ROW = kHeadDim * ES;              // bytes of one K/V row: 256 (bf16), 128 (fp8)
@@ -326,6 +331,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   float m = -__builtin_huge_valf();  // running reference maximum (log2 units)
   float l = 0.0f;                    // this lane's half of the row sum (rounded P)
   float lx = 0.0f;                   // fp8 with LSE: the same sum over unrounded P
+  // fp8: the row sum of the rounded P runs on the matrix core, as an all-ones A
+  // operand against the P^T operand: every row of this accumulator is the sum over
+  // keys for the lane's query column (replaces a decode and four adds per 4 keys).
+  f32x16 lacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) lacc[v] = 0.0f;
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -357,6 +368,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
       const float mnew = grow ? mx : m;
       const float al = __builtin_amdgcn_exp2f(m - mnew);
       l *= al;
+      if (DT == 1) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) lacc[v] *= al;
+      }
       if (DT == 1 && LSE) lx *= al;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -409,12 +424,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[t][v0 + e], c, -moff));
         if (LSE) lx += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+        // the first conversion writes the low half of pv[0]'s own register (dead
+        // afterwards), so no register has to be cleared first
+        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], __float_as_int(pv[0]), false);
         wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
         pf[q4] = wv;
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
-        l += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+      }
+      {
+        const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+        lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 0, 0, 0);
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -484,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnK p) {
   }
 
   // ---- epilogue: O = O^T / l, bf16 rows of 128 d per query
-  const float lt = half_swap_sum(l);
+  const float lt = DT == 1 ? lacc[0] : half_swap_sum(l);
   // LSE of the exact (unrounded) probabilities; fp8 P is rounded to e4m3 for the
   // product, so its normaliser lt differs from the exact sum by a few percent.
   const float lsum = (DT == 1 && LSE) ? half_swap_sum(lx) : lt;

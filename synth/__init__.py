@@ -322,10 +322,17 @@ def config_lengths(k: int) -> list:
     return [{0: 4096, 1: 32768, 2: 131072, 3: 262144}[k]]
 
 
-def make_config(k: int, threads: int = 8) -> Workload:
-    """Workload k of the five standard configurations (seed 1000 + k)."""
+def make_config(k: int, threads: int = 8, dtype: Optional[str] = None) -> Workload:
+    """Workload k of the five standard configurations (seed 1000 + k).  ``dtype="fp8"``
+    with k = 2 gives the 128K workload quantised the way the 256K fp8 one is (same
+    seed, so the same fp32 values before quantisation)."""
     seed = 1000 + k
     name = CONFIG_NAMES[k]
+    if dtype is not None and dtype != {3: "fp8"}.get(k, "bf16"):
+        if (k, dtype) != (2, "fp8"):
+            raise ValueError(f"config {k} has no {dtype} variant")
+        return make_workload("gqa32x4_L131072_fp8", 32, 4, [131072], seed=seed, dtype="fp8", vertical=20,
+                             alphas=(0.1,), n_sink=1, n_local=4, threads=threads)
     if k == 0:
         return make_workload(name, 1, 1, [4096], seed=seed, vertical=4, slash=False,
                              alphas=(0.1,), n_sink=1, n_local=2, threads=threads)
