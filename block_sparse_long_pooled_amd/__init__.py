@@ -337,6 +337,31 @@ def mean_correct(q, pooled_k, pooled_v, idx, counts, out, lse, q_scale=None, sof
     return out, lse
 
 
+def mean_correct_noalloc(q, pooled_k, pooled_v, idx, counts, out, lse, q_scale=None, softmax_scale=None):
+    """mean_correct without a workspace: the library's static per-GPU scratch (8 MiB)
+    holds the tile images, so nothing is allocated.  Calls that overlap on one GPU
+    race; sizes beyond the scratch raise FlashPrefillError (FP_EUNSUPPORTED)."""
+    _rows("q", q)
+    L, hq, d = q.shape
+    hkv = pooled_k.shape[0]
+    _heads(hq, hkv)
+    nb = _nb(L)
+    _scales(_dtype_code(q), q_scale=(q_scale, hq))
+    _pooled("pooled_k", pooled_k, hkv, nb)
+    _pooled("pooled_v", pooled_v, hkv, nb)
+    _lists(idx, counts, hq, nb, nb * (nb + 1) // 2)
+    _out_rows(out, L, hq)
+    _exact("lse", lse, (hq, L), torch.float32)
+    _require(lse is not None, "lse is required (the sparse call's return_lse=True output)")
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    _device(q, q_scale, pooled_k, pooled_v, idx, counts, out, lse)
+    call("fp_mean_correct_noalloc", _ptr(q), _dtype_code(q), _ptr(q_scale), _ptr(pooled_k), _ptr(pooled_v), L, hq,
+         hkv, d, BLOCK, q.stride(0), q.stride(1), out.stride(0), out.stride(1), _ptr(idx), _ptr(counts),
+         float(softmax_scale), _ptr(out), _ptr(lse), _stream(q))
+    return out, lse
+
+
 def union_compact(mask, hkv: int, idx=None, counts=None):
     """Group-shared lists: the union of the per-head masks (from threshold_mask) of
     every KV group, as ascending lists -> (idx [hkv * nb(nb+1)/2] int32,

@@ -144,7 +144,7 @@ const char* fp_status_string(int status) {
 
 const char* fp_last_error(void) { return g_last_error.c_str(); }
 
-int fp_abi_version(void) { return 2; }
+int fp_abi_version(void) { return 3; }
 
 int64_t fp_num_blocks(int64_t L, int block) { return block > 0 && L >= 0 ? (L + block - 1) / block : -1; }
 
@@ -338,21 +338,16 @@ int64_t fp_mean_correct_workspace_bytes(int L, int hkv) {
   return fp::meancorr_workspace_bytes(L, hkv);
 }
 
-int fp_mean_correct(const void* q, int dtype, const float* q_scale,
-                    const double* pooled_k, const double* pooled_v,
-                    int L, int hq, int hkv, int d, int block,
-                    int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
-                    const int32_t* idx, const int32_t* counts, float softmax_scale,
-                    void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+// Argument checks shared by both mean-correction entry points (workspace aside).
+static int meancorr_check(const void* q, int dtype, const float* q_scale, const double* pooled_k,
+                          const double* pooled_v, int L, int hq, int hkv, int d, int block,
+                          int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                          const int32_t* idx, const int32_t* counts, float softmax_scale, void* out, float* lse) {
   int r;
   if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
   if (L < 0) return fail(FP_EINVAL, "L < 0");
-  if (L == 0) return ok();
+  if (L == 0) return FP_OK;
   if ((r = check_tensor("q", q, dtype, q_stride_tok, q_stride_head))) return r;
-  if (workspace == nullptr || !aligned16(workspace)) return fail(FP_EINVAL, "workspace is NULL or not 16-byte aligned");
-  if (workspace_bytes < fp::meancorr_workspace_bytes(L, hkv))
-    return fail(FP_EINVAL, "workspace of %lld bytes < fp_mean_correct_workspace_bytes = %lld",
-                (long long)workspace_bytes, (long long)fp::meancorr_workspace_bytes(L, hkv));
   if ((r = check_tensor("out", out, FP_BF16, o_stride_tok, o_stride_head))) return r;
   if (pooled_k == nullptr || pooled_v == nullptr) return fail(FP_EINVAL, "pooled K/V is NULL");
   if (!aligned16(pooled_k) || !aligned16(pooled_v)) return fail(FP_EINVAL, "pooled K/V not 16-byte aligned");
@@ -364,8 +359,50 @@ int fp_mean_correct(const void* q, int dtype, const float* q_scale,
   if (dtype == FP_FP8_E4M3 && q_scale == nullptr) return fail(FP_EINVAL, "fp8 needs q_scale");
   if (!std::isfinite(softmax_scale) || softmax_scale <= 0.0f) return fail(FP_EINVAL, "softmax_scale must be > 0");
   if ((int64_t)hq * nblocks(L) >= (int64_t)1 << 31) return fail(FP_EINVAL, "grid too large");
+  return FP_OK;
+}
+
+int fp_mean_correct(const void* q, int dtype, const float* q_scale,
+                    const double* pooled_k, const double* pooled_v,
+                    int L, int hq, int hkv, int d, int block,
+                    int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                    const int32_t* idx, const int32_t* counts, float softmax_scale,
+                    void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+  int r;
+  if ((r = meancorr_check(q, dtype, q_scale, pooled_k, pooled_v, L, hq, hkv, d, block, q_stride_tok, q_stride_head,
+                          o_stride_tok, o_stride_head, idx, counts, softmax_scale, out, lse)))
+    return r;
+  if (L == 0) return ok();
+  if (workspace == nullptr || !aligned16(workspace)) return fail(FP_EINVAL, "workspace is NULL or not 16-byte aligned");
+  if (workspace_bytes < fp::meancorr_workspace_bytes(L, hkv))
+    return fail(FP_EINVAL, "workspace of %lld bytes < fp_mean_correct_workspace_bytes = %lld",
+                (long long)workspace_bytes, (long long)fp::meancorr_workspace_bytes(L, hkv));
   fp::MeanCorrLaunch a{q, q_scale, dtype, L, hq, hkv, q_stride_tok, q_stride_head, o_stride_tok, o_stride_head,
                        pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, workspace};
+  return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
+}
+
+int fp_mean_correct_noalloc(const void* q, int dtype, const float* q_scale,
+                            const double* pooled_k, const double* pooled_v,
+                            int L, int hq, int hkv, int d, int block,
+                            int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                            const int32_t* idx, const int32_t* counts, float softmax_scale,
+                            void* out, float* lse, void* stream) {
+  int r;
+  if ((r = meancorr_check(q, dtype, q_scale, pooled_k, pooled_v, L, hq, hkv, d, block, q_stride_tok, q_stride_head,
+                          o_stride_tok, o_stride_head, idx, counts, softmax_scale, out, lse)))
+    return r;
+  if (L == 0) return ok();
+  const int64_t need = fp::meancorr_workspace_bytes(L, hkv);
+  if (need > fp::meancorr_scratch_bytes())
+    return fail(FP_EUNSUPPORTED, "L=%d with hkv=%d needs %lld bytes of scratch; the library's static scratch holds "
+                "%lld (use fp_mean_correct with a caller workspace)", L, hkv, (long long)need,
+                (long long)fp::meancorr_scratch_bytes());
+  void* ws = nullptr;
+  hipError_t e = fp::meancorr_scratch(&ws);
+  if (e != hipSuccess) return fail(FP_EHIP, "static scratch address: %s", hipGetErrorString(e));
+  fp::MeanCorrLaunch a{q, q_scale, dtype, L, hq, hkv, q_stride_tok, q_stride_head, o_stride_tok, o_stride_head,
+                       pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, ws};
   return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
 }
 

@@ -111,6 +111,8 @@ struct MeanCorrLaunch {
 };
 hipError_t launch_meancorr(const MeanCorrLaunch& a, hipStream_t st);
 int meancorr_max_blocks();  // longest row the mean correction handles (blocks)
+int64_t meancorr_scratch_bytes();          // size of the library's static scratch
+hipError_t meancorr_scratch(void** ptr);   // its address on the current device
 int64_t meancorr_workspace_bytes(int L, int hkv);
 
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);

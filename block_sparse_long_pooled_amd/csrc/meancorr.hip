@@ -28,6 +28,8 @@
 //     the current one is computed.  S^T = (Kbar_hi + Kbar_lo) Q^T, O^T += Vbar^T P^T
 //     with P rounded to bf16 (the correction term carries ~2^-8 relative error); the
 //     row mass adds the unrounded P.
+#include <mutex>
+
 #include "fp_device.h"
 
 namespace fp {
@@ -307,6 +309,35 @@ __global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MCK p) {
 }
 
 }  // namespace
+
+// Scratch of the no-allocation entry point (fp_mean_correct_noalloc): room for the
+// tile images of hkv * ceil(nb / 32) <= 341 tiles, e.g. 4 KV heads up to 348K tokens.
+// Every GPU the library runs on holds its own copy until the process ends.  The
+// array's name is only a host-side stand-in: kernels get the device address taken
+// below, once per device.
+constexpr int64_t kScratchBytes = (int64_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int64_t meancorr_scratch_bytes() { return kScratchBytes; }
+
+hipError_t meancorr_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int meancorr_max_blocks() { return kMaxBlocks; }
 

@@ -78,7 +78,7 @@ enum fp_dtype {
 const char* fp_status_string(int status);
 /* Description of the last error returned on this host thread ("" if none). */
 const char* fp_last_error(void);
-/* Library ABI version (increments on any signature change; this header: 2). */
+/* Library ABI version (increments on any signature change; this header: 3). */
 int fp_abi_version(void);
 
 /* Host helpers: number of blocks ceil(L / block), and the idx capacity in
@@ -251,6 +251,31 @@ int fp_mean_correct(const void* q, int dtype, const float* q_scale,
 /* Workspace bytes fp_mean_correct needs for L tokens and hkv KV heads
  * (-1 for L < 0 or hkv < 1).  Host only. */
 int64_t fp_mean_correct_workspace_bytes(int L, int hkv);
+
+/* ---------------------------------------------------------------------------
+ * fp_mean_correct_noalloc -- fp_mean_correct for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same pass with its scratch taken from a static
+ * buffer inside the library instead of a caller workspace.  Nothing is
+ * allocated or freed by the call.
+ *   Limit: the scratch holds 8 MiB (8388608 bytes) per GPU, i.e. calls with
+ *   fp_mean_correct_workspace_bytes(L, hkv) <= 8388608 (e.g. hkv = 4 up to
+ *   348K tokens, hkv = 8 up to 174K); larger calls return FP_EUNSUPPORTED with
+ *   the sizes in fp_last_error() and enqueue nothing.
+ *   Sharing: every call on one GPU uses that GPU's single scratch buffer, which
+ *   keeps the last call's contents; the pass rewrites every byte it reads, so
+ *   nothing needs clearing, but calls that overlap on one GPU (concurrent
+ *   streams or host threads) race and must be serialised by the caller.
+ *   The buffer lives in the library's device code on every GPU it runs on until
+ *   the process ends.  Other arguments, numerics and errors as fp_mean_correct.
+ * ------------------------------------------------------------------------- */
+int fp_mean_correct_noalloc(const void* q, int dtype, const float* q_scale,
+                            const double* pooled_k, const double* pooled_v,
+                            int L, int hq, int hkv, int d, int block,
+                            int64_t q_stride_tok, int64_t q_stride_head,
+                            int64_t o_stride_tok, int64_t o_stride_head,
+                            const int32_t* idx, const int32_t* counts, float softmax_scale,
+                            void* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Group-shared lists (a PackGQA-style mode beyond the pages' per-head

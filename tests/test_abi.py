@@ -228,6 +228,23 @@ def test_pool_and_mean_correct_reject():
     assert lib.fp_mean_correct(*too_long) == EUNSUP
 
 
+def test_mean_correct_noalloc_rejects():
+    """The static-scratch variant rejects, before touching a GPU, calls whose tile
+    images exceed its 8 MiB scratch, and the usual malformed arguments."""
+    lib = _lib.load()
+    args = [P, 0, None, P, P, 1024, 4, 2, 128, 128, 512, 128, 512, 128, P, P, 0.088, P, P, None]
+    big = list(args); big[5] = 400 * 1024; big[7] = 4  # 4 KV heads x 98 tiles x 24 KB > 8 MiB
+    assert lib.fp_mean_correct_workspace_bytes(big[5], 4) > 8 << 20
+    assert lib.fp_mean_correct_noalloc(*big) == EUNSUP
+    assert b"scratch" in lib.fp_last_error() and b"8388608" in lib.fp_last_error()
+    bad_lse = list(args); bad_lse[18] = None
+    assert lib.fp_mean_correct_noalloc(*bad_lse) == EINVAL and b"lse" in lib.fp_last_error()
+    bad_d = list(args); bad_d[8] = 96
+    assert lib.fp_mean_correct_noalloc(*bad_d) == EUNSUP
+    empty = list(args); empty[5] = 0
+    assert lib.fp_mean_correct_noalloc(*empty) == _lib.FP_OK
+
+
 def test_empty_inputs_are_a_no_op():
     """L = 0 validates and returns FP_OK without launching anything."""
     assert discover(L=0) == _lib.FP_OK
