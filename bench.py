@@ -12,8 +12,13 @@ Prints ONE JSON line.  `value` is dense-equivalent TFLOP/s of the whole step
 (2 * hq * d * L^2 causal flops / step time).  `roofline` is for the dominant
 kernel (the sparse attention): computed MFMA flops per launch
 (sum(counts) * 4 * B^2 * d) over its mean launch time, measured with HIP
-events on the stream the kernels run on.  `cpu_baseline` times the fp64
-oracle on a bounded sample of the same workload on the host cores.
+events on the stream the kernels run on, against the datasheet peak and against
+the peak a pure matrix-core loop reaches on the same GPU.  `extra` carries the
+other workloads (the 4K config, the 32K config at three alphas, fp8 at 128K and
+256K, the paged batch) each beside the same-GPU dense kernel, and the next rows
+(logical skip, group-shared lists, mean correction, chunked prefill).
+`cpu_baseline` times the fp64 oracle on a stratified sample of the same workload
+with a process pool over the host cores.
 """
 from __future__ import annotations
 
@@ -42,22 +47,25 @@ def parse():
                          "8-sequence batch is measured in extra.paged_batch of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the same-GPU dense comparison")
-    ap.add_argument("--no-extra", action="store_true", help="skip the fp8 256K side measurement")
+    ap.add_argument("--no-extra", action="store_true", help="skip the paged-batch and fp8 256K side measurements")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the logical-skip (masked loop over every block) measurement")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of sampled oracle attention")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="wall seconds of sampled oracle attention (sparse and dense legs together)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 4K / 32K-alpha-sweep / fp8-128K side lines")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter scale reference)")
     return ap.parse_args()
 
 
-def counter_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary (already scaled by the copy calibration), or None when the attention
-    kernel source has changed since the counters were taken."""
+def counter_traffic(profile):
+    """HBM bytes per attention launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary under profiles/ (already scaled by the copy calibration), or None when the
+    attention kernel source has changed since the counters were taken."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    prof = os.path.join(root, "profiles", "attn_128k_bf16_hbm_traffic.txt")
+    prof = os.path.join(root, "profiles", profile)
     src = os.path.join(root, "block_sparse_long_pooled_amd", "csrc", "attn.hip")
     try:
         fields = dict(line.split(":", 1) for line in open(prof) if ":" in line and not line.startswith("#"))
@@ -378,16 +386,135 @@ def time_dense(tensors, reps=2):
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(wl, alpha, dense_eq_flops, budget_s):
-    """fp64 oracle on the host: pooling, scores, threshold and lists on the whole
-    input; sparse attention on seeded sampled (head, query block) rows within a time
-    budget, extrapolated to all rows by the number of listed blocks."""
-    import oracle as O
+def measured_peaks():
+    """Peaks a pure matrix-core loop (bf16 and fp8 products on register operands, one
+    wave per SIMD) and a streaming read of 4 GiB reach on this GPU (libfppeaks.so)."""
+    import ctypes
+
+    import torch
+
+    import block_sparse_long_pooled_amd as fp
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(fp.__file__), "libfppeaks.so"))
+    lib.fpk_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fpk_mfma_loop_flops.restype = ctypes.c_double
+    lib.fpk_mfma_loop_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.fpk_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    st = torch.cuda.current_stream(dev).cuda_stream
+    sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    res = {"compute_units": cus}
+    for dt, name, iters in ((0, "mfma_bf16_tflops", 20000), (1, "mfma_fp8_tflops", 10000)):
+        ms = timed(lambda: lib.fpk_mfma_loop(dt, cus, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)))
+        res[name] = lib.fpk_mfma_loop_flops(dt, cus, iters) / (ms * 1e-3) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    word = torch.zeros(1, dtype=torch.int32, device=dev)
+    ms = timed(lambda: lib.fpk_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), cus * 8,
+                                           ctypes.c_void_p(word.data_ptr()), ctypes.c_void_p(st)))
+    res["stream_read_gbs"] = buf.numel() / (ms * 1e-3) / 1e9
+    del buf
+    res["note"] = ("one 4-wave workgroup per CU of back-to-back independent 32x32 products on register "
+                   "operands; 16-byte non-temporal loads over 4 GiB")
+    return res
+
+
+def roofline_block(kernel, computed_flops, ms, dtype, peaks, traffic=None):
+    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP8_TFLOPS
+    achieved = computed_flops / (ms * 1e-3) / 1e12
+    meas = peaks.get("mfma_bf16_tflops" if dtype == "bf16" else "mfma_fp8_tflops") if peaks else None
+    return {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic,
+            "peak_measured": meas, "frac_measured": (achieved / meas) if meas else None}
+
+
+def workload_line(wl, alpha, steps, warmup, peaks, dense=True):
+    """One workload's hot path (per-stage HIP events) beside the same-GPU dense kernel."""
+    import torch
+    r = time_hot_path(wl, steps, warmup, alpha)
+    nb, hq, d, L = r["nb"], wl.hq, wl.d, wl.L
+    comp = r["sum_counts"] * 4.0 * BLOCK * BLOCK * d
+    dense_eq = 2.0 * hq * d * L * L
+    line = {
+        "workload": wl.name, "alpha": alpha, "n_sink": wl.n_sink, "n_local": wl.n_local,
+        "density": r["sum_counts"] / (hq * nb * (nb + 1) / 2),
+        "stage_ms": dict(zip(("discover", "threshold_compact", "sparse_attn"), r["stage_median"])),
+        "ms_per_step": r["ms_per_step"],
+        "dense_equiv_tflops": dense_eq / (r["ms_per_step"] * 1e-3) / 1e12,
+        "roofline": roofline_block(f"attn_kernel (sparse, {wl.dtype})", comp, r["stage_median"][2], wl.dtype, peaks),
+    }
+    if dense:
+        dms = time_dense(r["tensors"], reps=1 if L > 131072 else 2)
+        line["dense_attn_ms"] = dms
+        line["dense_attn_frac"] = dense_eq / (dms * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS if wl.dtype == "bf16"
+                                                                      else PEAK_FP8_TFLOPS)
+        line["speedup_vs_dense_step"] = dms / r["ms_per_step"]
+    del r["tensors"], r["pooled"], r["lists"]
+    torch.cuda.empty_cache()
+    return line
+
+
+# --------------------------------------------------------------- CPU baseline
+_CPU = {}
+
+
+def _cpu_worker_init():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
+
+
+def _cpu_rows(task):
+    """Oracle attention for a chunk of (head, query block) rows; returns
+    (seconds, listed blocks computed).  Runs in a pool worker."""
+    import oracle as O
+    rows, dense = task
+    q, k, v, lists = _CPU["q"], _CPU["k"], _CPU["v"], _CPU["lists"]
+    t = time.perf_counter()
+    blocks = 0
+    for h, i in rows:
+        blocks_i = np.arange(i + 1) if dense else lists[h][i]
+        O.attend_block(q, k, v, blocks_i, h, i, BLOCK)
+        blocks += len(blocks_i)
+    return time.perf_counter() - t, blocks
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, alpha, dense_eq_flops, budget_s):
+    """The fp64 oracle on the host: pooling, scores, threshold and lists on the whole
+    input (one process), then sparse attention (over the oracle's lists) and dense
+    attention on a stratified sample of (head, query block) rows -- every head, query
+    blocks drawn at random per head -- run by a process pool with one worker per core
+    (up to 16) and BLAS at one thread per worker.  Each leg's worker seconds are
+    extrapolated to all rows by listed (sparse) or causal (dense) block count and
+    divided by the worker count."""
+    import multiprocessing as mp
+
+    import oracle as O
     q = O.decode_bf16(wl.q) if wl.dtype == "bf16" else O.dequantize(wl.q, wl.q_scale)
     k = O.decode_bf16(wl.k) if wl.dtype == "bf16" else O.dequantize(wl.k, wl.k_scale)
     v = O.decode_bf16(wl.v) if wl.dtype == "bf16" else O.dequantize(wl.v, wl.v_scale)
@@ -396,33 +523,47 @@ def cpu_baseline(wl, alpha, dense_eq_flops, budget_s):
     t_sel = time.perf_counter() - t
     counts = sel["counts"]
     hq, nb = counts.shape
+    _CPU.update(q=q, k=k, v=v, lists=sel["lists"])
+    workers = max(1, min(os.cpu_count() or 1, 16))
     rng = np.random.default_rng(12345)
-    order = rng.permutation(hq * nb)
-    t_att = 0.0
-    done_blocks = 0
-    rows = 0
-    for r in order:
-        h, i = divmod(int(r), nb)
-        t = time.perf_counter()
-        O.attend_block(q, k, v, sel["lists"][h][i], h, i, BLOCK)
-        t_att += time.perf_counter() - t
-        done_blocks += int(counts[h, i])
-        rows += 1
-        if t_att >= budget_s:
-            break
-    total_blocks = int(counts.sum())
-    t_att_all = t_att * total_blocks / max(done_blocks, 1)
-    t_all = t_sel + t_att_all
+    perm = [rng.permutation(nb) for _ in range(hq)]
+    legs = {}
+    with mp.get_context("fork").Pool(workers, initializer=_cpu_worker_init) as pool:
+        for dense in (False, True):
+            t0 = time.perf_counter()
+            secs = blocks = n_rows = 0
+            rnd = 0
+            while time.perf_counter() - t0 < budget_s / 2 and rnd < nb:
+                # one round: every head, `workers` new query blocks each, in chunks of 4 rows
+                rows = [(h, int(perm[h][j])) for j in range(rnd, min(rnd + workers, nb)) for h in range(hq)]
+                rnd += workers
+                tasks = [(rows[c:c + 4], dense) for c in range(0, len(rows), 4)]
+                for sec, blk in pool.imap_unordered(_cpu_rows, tasks):
+                    secs += sec
+                    blocks += blk
+                n_rows += len(rows)
+            total = nb * (nb + 1) // 2 * hq if dense else int(counts.sum())
+            legs["dense" if dense else "sparse"] = dict(worker_s=secs, rows=n_rows, blocks=blocks,
+                                                        wall_all_s=secs * total / max(blocks, 1) / workers)
+    _CPU.clear()
+    t_all = t_sel + legs["sparse"]["wall_all_s"]
+    sp, de = legs["sparse"], legs["dense"]
     return {
         "value": dense_eq_flops / t_all / 1e12,
-        "unit": "TFLOP/s (dense-equivalent)",
-        "cores": int(cores),
+        "unit": "TFLOP/s (dense-equivalent, whole hot path)",
+        "cores": workers,
         "kind": "oracle",
         "ms_per_step": t_all * 1e3,
-        "sample": (f"fp64 oracle: pooling+scores+threshold+lists on all {hq}x{nb} rows ({t_sel:.1f} s); "
-                   f"sparse attention on {rows} seeded random (head, query-block) rows = "
-                   f"{100.0 * done_blocks / total_blocks:.2f}% of listed blocks ({t_att:.1f} s), "
-                   f"extrapolated by listed-block count"),
+        "host_cpu_count": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "dense_oracle": {"ms": de["wall_all_s"] * 1e3,
+                         "tflops": dense_eq_flops / de["wall_all_s"] / 1e12},
+        "sample": (f"extrapolated: fp64 oracle with {workers} worker processes (BLAS 1 thread each); "
+                   f"pooling+scores+threshold+lists on all {hq}x{nb} rows in one process ({t_sel:.1f} s); "
+                   f"sparse attention on {sp['rows']} (head, query-block) rows = every head x "
+                   f"{sp['rows'] // hq} random query blocks, {100.0 * sp['blocks'] / max(int(counts.sum()), 1):.2f}% "
+                   f"of listed blocks ({sp['worker_s']:.1f} worker-s); dense attention on {de['rows']} rows "
+                   f"({de['worker_s']:.1f} worker-s); each leg extrapolated by block count"),
     }
 
 
@@ -435,6 +576,14 @@ def main():
     import torch  # noqa: F401
 
     import synth
+
+    peaks = {}
+    try:
+        peaks = measured_peaks()
+        log(f"measured peaks: bf16 MFMA loop {peaks['mfma_bf16_tflops']:.0f} TFLOP/s, fp8 "
+            f"{peaks['mfma_fp8_tflops']:.0f} TFLOP/s, streaming read {peaks['stream_read_gbs']:.0f} GB/s")
+    except OSError as e:  # the peaks library is optional: fractions then use the datasheet only
+        log(f"no measured peaks ({e})")
 
     t = time.perf_counter()
     wl = synth.make_config(args.config)
@@ -465,7 +614,10 @@ def main():
         "discover_hbm_frac": disc_gbs / PEAK_HBM_GBS,
         "selection_overhead_frac": (r["disc_ms"] + r["thr_ms"]) / r["ms_per_step"],
         "stage_ms_median": dict(zip(("discover", "threshold_compact", "sparse_attn"), r["stage_median"])),
+        "measured_peaks": peaks,
     }
+    if peaks:
+        extra["discover_stream_frac"] = disc_gbs / peaks["stream_read_gbs"]
     dcold = time_discover_cold(r)
     extra["discover_cold_cache"] = {"ms": dcold, "gbs": disc_bytes / (dcold * 1e-3) / 1e9,
                                     "hbm_frac": disc_bytes / (dcold * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -510,31 +662,34 @@ def main():
             f"attention {pb['paged']['mfma_frac'] * 100:.1f}% of MFMA peak")
         torch.cuda.empty_cache()
         wl8 = synth.make_config(3)
-        r8 = time_hot_path(wl8, max(2, args.steps // 2), 1, wl8.alphas[0])
-        nb8 = r8["nb"]
-        L8 = wl8.L
-        c8 = r8["sum_counts"] * 4.0 * BLOCK * BLOCK * d
-        extra["fp8_256k"] = {
-            "workload": wl8.name, "ms_per_step": r8["ms_per_step"],
-            "dense_equiv_tflops": 2.0 * wl8.hq * d * L8 * L8 / (r8["ms_per_step"] * 1e-3) / 1e12,
-            "stage_ms": {"discover": r8["disc_ms"], "threshold_compact": r8["thr_ms"], "sparse_attn": r8["attn_ms"]},
-            "density": r8["sum_counts"] / (wl8.hq * nb8 * (nb8 + 1) / 2),
-            "attn_computed_tflops": c8 / (r8["attn_ms"] * 1e-3) / 1e12,
-            "mfma_frac_fp8": c8 / (r8["attn_ms"] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-        }
-        if not args.no_dense:
-            # the same-GPU dense fp8 kernel on the same inputs (dense-equivalent causal
-            # work 2 hq d L^2, as for the bf16 dense figure)
-            dm8 = time_dense(r8["tensors"], reps=1)
-            dense8 = 2.0 * wl8.hq * d * L8 * L8
-            extra["fp8_256k"].update({
-                "dense_attn_ms": dm8,
-                "dense_attn_mfma_frac_fp8": dense8 / (dm8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                "speedup_vs_dense_step": dm8 / r8["ms_per_step"],
-            })
-            log(f"fp8 256K dense attention {dm8:.1f} ms")
-        del r8["tensors"], r8["pooled"], r8["lists"], wl8
-        log(f"fp8 256K step {extra['fp8_256k']['ms_per_step']:.2f} ms")
+        f8 = workload_line(wl8, wl8.alphas[0], max(2, args.steps // 2), 1, peaks, dense=not args.no_dense)
+        f8["roofline"]["traffic"] = counter_traffic("attn_256k_fp8_hbm_traffic.txt")
+        extra["fp8_256k"] = f8
+        del wl8
+        log(f"fp8 256K step {f8['ms_per_step']:.2f} ms, attention {f8['roofline']['frac'] * 100:.1f}% of fp8 peak")
+
+    if not args.no_configs and args.config == 2:
+        import torch
+        # the other workloads, each beside the same-GPU dense kernel: the 4K config,
+        # the 32K config at its three alphas, and the 128K workload quantised to fp8
+        lines = {}
+        wl0 = synth.make_config(0)
+        lines["tiny_4k"] = workload_line(wl0, wl0.alphas[0], args.steps, args.warmup, peaks, dense=not args.no_dense)
+        wl1 = synth.make_config(1)
+        for a1 in wl1.alphas:
+            lines[f"gqa28x4_32k_alpha{a1}"] = workload_line(wl1, a1, args.steps, args.warmup, peaks,
+                                                            dense=not args.no_dense)
+        del wl1
+        wlf = synth.make_config(2, dtype="fp8")
+        lines["fp8_128k"] = workload_line(wlf, wlf.alphas[0], max(2, args.steps // 2), 1, peaks,
+                                          dense=not args.no_dense)
+        del wlf
+        torch.cuda.empty_cache()
+        for name, ln in lines.items():
+            log(f"{name}: step {ln['ms_per_step']:.3f} ms, density {ln['density']:.3f}, attention "
+                f"{ln['roofline']['frac'] * 100:.1f}% of peak"
+                + (f", {ln['speedup_vs_dense_step']:.2f}x the dense kernel" if "speedup_vs_dense_step" in ln else ""))
+        extra["configs"] = lines
 
     line = {
         "metric": "prefill attn ms & dense-equiv TFLOP/s at 128K GQA bf16/fp8; MFMA util",
@@ -552,12 +707,8 @@ def main():
         "config": {"workload": wl.name, "hq": hq, "hkv": hkv, "head_dim": d, "seq_len": L, "block": BLOCK,
                    "alpha": alpha, "n_sink": wl.n_sink, "n_local": wl.n_local, "batch": 1,
                    "step": "discover + threshold_compact + sparse_attn"},
-        "roofline": {
-            "kernel": "attn_kernel (sparse, bf16)" if wl.dtype == "bf16" else "attn_kernel (sparse, fp8)",
-            "bound": "mfma", "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": attn_tflops / peak,
-            "traffic": counter_traffic() if (args.config == 2) else None,
-        },
+        "roofline": roofline_block(f"attn_kernel (sparse, {wl.dtype})", computed_flops, r["attn_ms"], wl.dtype, peaks,
+                                   counter_traffic("attn_128k_bf16_hbm_traffic.txt") if args.config == 2 else None),
         "extra": extra,
     }
     if args.calibrate:
