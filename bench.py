@@ -257,7 +257,28 @@ def time_paged_batch(alpha, reps=3):
             "attn_computed_tflops": comp, "mfma_frac": comp / PEAK_BF16_TFLOPS,
         }
     res["density"] = tiles / sum(wl.hq * (-(-n // BLOCK)) * (-(-n // BLOCK) + 1) / 2 for n in wl.lengths)
-    del q, k, v, kc, vc, out
+    # the V2 mean correction (an assumption) over the whole batch: pool V per
+    # sequence through the page table, then correct every sequence in place
+    pq, pk = fp.discover_paged(q, kc, batch, page_table=table)
+    idx, counts = fp.threshold_compact_varlen(pq, pk, batch, alpha, wl.n_sink, wl.n_local)
+    o_s, lse = fp.sparse_attn_paged(q, kc, vc, batch, idx, counts, page_table=table, return_lse=True)
+    ws = torch.empty(int(fp.load().fp_mean_correct_varlen_workspace_bytes(batch.total_blocks, batch.n_seqs, wl.hkv)),
+                     dtype=torch.uint8, device=dev)
+    pv = fp.pool_varlen(vc, batch, page_table=table)
+    o_c, l_c = o_s.clone(), lse.clone()
+    fp.mean_correct_varlen(q, pk, pv, batch, idx, counts, o_c, l_c, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    fp.pool_varlen(vc, batch, page_table=table, pooled=pv)
+    ev[1].record()
+    fp.mean_correct_varlen(q, pk, pv, batch, idx, counts, o_c, l_c, workspace=ws)
+    ev[2].record()
+    torch.cuda.synchronize()
+    res["mean_correction"] = {"pool_v_ms": ev[0].elapsed_time(ev[1]), "correct_ms": ev[1].elapsed_time(ev[2]),
+                              "note": "assumption: pruned blocks enter the softmax as 128 copies of their mean "
+                                      "key/value; every sequence of the batch, V pooled through the page table"}
+    del q, k, v, kc, vc, out, o_s, o_c, lse, l_c, ws
     return res
 
 

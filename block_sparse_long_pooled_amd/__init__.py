@@ -557,6 +557,60 @@ def sparse_attn_paged(q, k, v, batch: VarlenBatch, idx=None, counts=None, page_t
     return (out, lse) if return_lse else out
 
 
+def pool_varlen(x, batch: VarlenBatch, page_table=None, scale=None, pooled=None):
+    """Per-sequence block means of packed x [T, H, 128] or of a page cache [P, 128, H, 128]
+    -> [H, total_blocks, 128] fp64 (used to pool V for mean_correct_varlen)."""
+    _kv_batch("x", x, page_table, batch.total_tokens)
+    _page_table(page_table, batch.n_seqs, _nb(batch.max_seqlen))
+    if page_table is not None:
+        P, _, H, d = x.shape
+        st = (x.stride(0), x.stride(1), x.stride(2))
+        max_pages = page_table.shape[1]
+    else:
+        P, H, d = 0, x.shape[1], x.shape[2]
+        st = (0, x.stride(0), x.stride(1))
+        max_pages = 0
+    _scales(_dtype_code(x), scale=(scale, H))
+    if pooled is None:
+        pooled = torch.empty((H, batch.total_blocks, d), dtype=torch.float64, device=x.device)
+    _pooled("pooled", pooled, H, batch.total_blocks)
+    _device(x, page_table, scale, pooled, batch.cu_seqlens)
+    call("fp_pool_varlen", _ptr(x), _dtype_code(x), _ptr(scale), _ptr(batch.cu_seqlens), batch.n_seqs,
+         batch.max_seqlen, batch.total_tokens, batch.total_blocks, _ptr(page_table), max_pages, P, H, d, BLOCK, *st,
+         _ptr(pooled), _stream(x))
+    return pooled
+
+
+def mean_correct_varlen(q, pooled_k, pooled_v, batch: VarlenBatch, idx, counts, out, lse, q_scale=None,
+                        softmax_scale=None, workspace=None):
+    """mean_correct applied to every sequence of a packed batch, in place on the output
+    and LSE of sparse_attn_paged(..., return_lse=True).  pooled_k from discover_paged,
+    pooled_v from pool_varlen, idx/counts from threshold_compact_varlen."""
+    _rows("q", q, tokens=batch.total_tokens)
+    T, hq, d = q.shape
+    hkv = pooled_k.shape[0]
+    _heads(hq, hkv)
+    _scales(_dtype_code(q), q_scale=(q_scale, hq))
+    _pooled("pooled_k", pooled_k, hkv, batch.total_blocks)
+    _pooled("pooled_v", pooled_v, hkv, batch.total_blocks)
+    _lists(idx, counts, hq, batch.total_blocks, batch.total_tri)
+    _out_rows(out, T, hq)
+    _require(lse is not None, "lse is required (the sparse call's return_lse=True output)")
+    _exact("lse", lse, (hq, T), torch.float32)
+    if softmax_scale is None:
+        softmax_scale = default_scale(d)
+    need = int(load().fp_mean_correct_varlen_workspace_bytes(batch.total_blocks, max(batch.n_seqs, 1), hkv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _capacity("workspace", workspace, need, torch.uint8)
+    _device(q, q_scale, pooled_k, pooled_v, idx, counts, out, lse, workspace, batch.cu_seqlens)
+    call("fp_mean_correct_varlen", _ptr(q), _dtype_code(q), _ptr(q_scale), _ptr(pooled_k), _ptr(pooled_v),
+         _ptr(batch.cu_seqlens), batch.n_seqs, batch.max_seqlen, batch.total_tokens, batch.total_blocks,
+         batch.total_tri, hq, hkv, d, BLOCK, q.stride(0), q.stride(1), out.stride(0), out.stride(1), _ptr(idx),
+         _ptr(counts), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(q))
+    return out, lse
+
+
 # --------------------------------------------------------------- chunked prefill
 @dataclass
 class ChunkedBatch:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FLASHPREFILL_LIB") or os.path.join(HERE, "libflashprefill.so")
 
 FP_OK, FP_EINVAL, FP_EUNSUPPORTED, FP_EHIP = 0, 1, 2, 3
-ABI_VERSION = 3  # the signatures below; the library must report the same version
+ABI_VERSION = 4  # the signatures below; the library must report the same version
 FP_BF16, FP_FP8_E4M3 = 0, 1
 
 
@@ -50,6 +50,12 @@ _SIGNATURES = {
     "fp_mean_correct": (c_int, [_p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                 _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p, _i64, _p]),
     "fp_mean_correct_workspace_bytes": (c_int64, [c_int, c_int]),
+    "fp_mean_correct_varlen": (c_int, [_p, c_int, _p, _p, _p, _p, c_int, c_int, _i64, _i64, _i64,
+                                       c_int, c_int, c_int, c_int, _i64, _i64, _i64, _i64, _p, _p, c_float,
+                                       _p, _p, _p, _i64, _p]),
+    "fp_mean_correct_varlen_workspace_bytes": (c_int64, [c_int64, c_int, c_int]),
+    "fp_pool_varlen": (c_int, [_p, c_int, _p, _p, c_int, c_int, _i64, _i64, _p, c_int, c_int, c_int, c_int, c_int,
+                               _i64, _i64, _i64, _p, _p]),
     "fp_mean_correct_noalloc": (c_int, [_p, c_int, _p, _p, _p, c_int, c_int, c_int, c_int, c_int,
                                         _i64, _i64, _i64, _i64, _p, _p, c_float, _p, _p, _p]),
     "fp_union_compact": (c_int, [_p, c_int, c_int, c_int, _p, _p, _p]),

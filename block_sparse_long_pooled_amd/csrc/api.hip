@@ -144,7 +144,7 @@ const char* fp_status_string(int status) {
 
 const char* fp_last_error(void) { return g_last_error.c_str(); }
 
-int fp_abi_version(void) { return 3; }
+int fp_abi_version(void) { return 4; }
 
 int64_t fp_num_blocks(int64_t L, int block) { return block > 0 && L >= 0 ? (L + block - 1) / block : -1; }
 
@@ -377,8 +377,8 @@ int fp_mean_correct(const void* q, int dtype, const float* q_scale,
   if (workspace_bytes < fp::meancorr_workspace_bytes(L, hkv))
     return fail(FP_EINVAL, "workspace of %lld bytes < fp_mean_correct_workspace_bytes = %lld",
                 (long long)workspace_bytes, (long long)fp::meancorr_workspace_bytes(L, hkv));
-  fp::MeanCorrLaunch a{q, q_scale, dtype, L, hq, hkv, q_stride_tok, q_stride_head, o_stride_tok, o_stride_head,
-                       pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, workspace};
+  fp::MeanCorrLaunch a{q, q_scale, dtype, single_seq(L), fp::meancorr_tiles(L), hq, hkv, q_stride_tok, q_stride_head,
+                       o_stride_tok, o_stride_head, pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, workspace};
   return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
 }
 
@@ -401,9 +401,69 @@ int fp_mean_correct_noalloc(const void* q, int dtype, const float* q_scale,
   void* ws = nullptr;
   hipError_t e = fp::meancorr_scratch(&ws);
   if (e != hipSuccess) return fail(FP_EHIP, "static scratch address: %s", hipGetErrorString(e));
-  fp::MeanCorrLaunch a{q, q_scale, dtype, L, hq, hkv, q_stride_tok, q_stride_head, o_stride_tok, o_stride_head,
-                       pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, ws};
+  fp::MeanCorrLaunch a{q, q_scale, dtype, single_seq(L), fp::meancorr_tiles(L), hq, hkv, q_stride_tok, q_stride_head,
+                       o_stride_tok, o_stride_head, pooled_k, pooled_v, idx, counts, softmax_scale, out, lse, ws};
   return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
+}
+
+int64_t fp_mean_correct_varlen_workspace_bytes(int64_t total_blocks, int n_seqs, int hkv) {
+  if (total_blocks < 0 || n_seqs < 1 || hkv < 1) return -1;
+  return (int64_t)hkv * fp::meancorr_tiles_varlen(total_blocks, n_seqs) * fp::meancorr_tile_bytes();
+}
+
+int fp_mean_correct_varlen(const void* q, int dtype, const float* q_scale,
+                           const double* pooled_k, const double* pooled_v,
+                           const int32_t* cu_seqlens, int n_seqs, int max_seqlen,
+                           int64_t total_tokens, int64_t total_blocks, int64_t total_tri,
+                           int hq, int hkv, int d, int block,
+                           int64_t q_stride_tok, int64_t q_stride_head, int64_t o_stride_tok, int64_t o_stride_head,
+                           const int32_t* idx, const int32_t* counts, float softmax_scale,
+                           void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+  int r;
+  fp::SeqDesc sd{};
+  if ((r = check_shape(dtype, hq, hkv, d, block))) return r;
+  if ((r = check_varlen(cu_seqlens, n_seqs, max_seqlen, total_tokens, total_blocks, total_tri, hq, &sd))) return r;
+  // the per-sequence checks of the single-sequence call, with the longest sequence
+  if ((r = meancorr_check(q, dtype, q_scale, pooled_k, pooled_v, max_seqlen, hq, hkv, d, block, q_stride_tok,
+                          q_stride_head, o_stride_tok, o_stride_head, idx, counts, softmax_scale, out, lse)))
+    return r;
+  if (total_tokens == 0 || sd.max_nb == 0) return ok();
+  const int64_t need = (int64_t)hkv * fp::meancorr_tiles_varlen(total_blocks, n_seqs) * fp::meancorr_tile_bytes();
+  if (workspace == nullptr || !aligned16(workspace)) return fail(FP_EINVAL, "workspace is NULL or not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FP_EINVAL, "workspace of %lld bytes < fp_mean_correct_varlen_workspace_bytes = %lld",
+                (long long)workspace_bytes, (long long)need);
+  fp::MeanCorrLaunch a{q, q_scale, dtype, sd, fp::meancorr_tiles_varlen(total_blocks, n_seqs), hq, hkv,
+                       q_stride_tok, q_stride_head, o_stride_tok, o_stride_head, pooled_k, pooled_v, idx, counts,
+                       softmax_scale, out, lse, workspace};
+  return launch_status(fp::launch_meancorr(a, (hipStream_t)stream));
+}
+
+int fp_pool_varlen(const void* x, int dtype, const float* scale, const int32_t* cu_seqlens, int n_seqs,
+                   int max_seqlen, int64_t total_tokens, int64_t total_blocks,
+                   const int32_t* page_table, int max_pages, int num_pages, int H, int d, int block,
+                   int64_t stride_page, int64_t stride_tok, int64_t stride_head, double* pooled, void* stream) {
+  int r;
+  if ((r = check_shape(dtype, H, H, d, block))) return r;
+  fp::SeqDesc sd{};
+  if ((r = check_varlen(cu_seqlens, n_seqs, max_seqlen, total_tokens, total_blocks, 0, H, &sd))) return r;
+  if (total_tokens == 0 || sd.max_nb == 0) return ok();
+  if ((r = check_tensor("x", x, dtype, stride_tok, stride_head))) return r;
+  fp::PageDesc pd{page_table, max_pages, num_pages};
+  if (page_table != nullptr) {
+    if ((r = check_tensor("x", x, dtype, stride_page, 0))) return r;
+    if (max_pages < sd.max_nb) return fail(FP_EINVAL, "max_pages=%d < ceil(max_seqlen/128)=%d", max_pages, sd.max_nb);
+    if (num_pages < 1) return fail(FP_EINVAL, "num_pages < 1");
+  }
+  if (pooled == nullptr || !aligned16(pooled)) return fail(FP_EINVAL, "pooled output is NULL or not 16-byte aligned");
+  if (dtype == FP_FP8_E4M3 && scale == nullptr) return fail(FP_EINVAL, "fp8 needs a per-head scale");
+  fp::PoolLaunch a{};
+  a.query_view = false;
+  a.dtype = dtype;
+  a.x = x; a.scale = scale; a.H = H; a.st_page = stride_page; a.st_tok = stride_tok; a.st_head = stride_head;
+  a.paged = page_table != nullptr;
+  a.out = pooled;
+  return launch_status(fp::launch_pool(a, sd, pd, (hipStream_t)stream));
 }
 
 int fp_union_compact(const uint32_t* mask, int nb, int hq, int hkv, int32_t* idx, int32_t* counts, void* stream) {

@@ -98,22 +98,27 @@ struct MeanCorrLaunch {
   const void* q;
   const float* q_scale;
   int dtype;
-  int L, hq, hkv;
+  SeqDesc sd;                 // one sequence (cu_seqlens == nullptr) or a packed batch
+  int64_t total_tiles;        // tile images per KV head in the workspace (its stride)
+  int hq, hkv;
   int64_t q_st, q_sh, o_st, o_sh;
-  const double* pooled_k;     // [hkv, nb, d]
-  const double* pooled_v;     // [hkv, nb, d]
+  const double* pooled_k;     // [hkv, total_blocks, d]
+  const double* pooled_v;     // [hkv, total_blocks, d]
   const int32_t* idx;         // per-head lists of the sparse call
   const int32_t* counts;
   float softmax_scale;
   void* out;                  // bf16 [L, hq, d], in and out
   float* lse;                 // [hq, L], in and out
-  void* workspace;            // meancorr_workspace_bytes(L, hkv) bytes, 16-byte aligned
+  void* workspace;            // hkv * total_tiles tile images, 16-byte aligned
 };
 hipError_t launch_meancorr(const MeanCorrLaunch& a, hipStream_t st);
 int meancorr_max_blocks();  // longest row the mean correction handles (blocks)
 int64_t meancorr_scratch_bytes();          // size of the library's static scratch
 hipError_t meancorr_scratch(void** ptr);   // its address on the current device
 int64_t meancorr_workspace_bytes(int L, int hkv);
+int64_t meancorr_tiles(int L);                                   // tile images per KV head, one sequence
+int64_t meancorr_tiles_varlen(int64_t total_blocks, int n_seqs);  // upper bound for a packed batch
+int64_t meancorr_tile_bytes();
 
 hipError_t launch_pool(const PoolLaunch& a, const SeqDesc& sd, const PageDesc& pd, hipStream_t st);
 hipError_t launch_select(const SelectLaunch& a, const SeqDesc& sd, hipStream_t st);

@@ -59,13 +59,32 @@ __device__ inline int vt_slot(int k16) { return 8 * ((k16 >> 2) & 1) + 4 * (k16 
 __device__ inline unsigned k_pos(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) * 16); }
 __device__ inline unsigned vt_pos(int d, int chunk) { return 2 * kTile * 256 + d * 64 + ((chunk ^ ((d >> 2) & 3)) * 16); }
 
-__global__ __launch_bounds__(kThreads) void meanprep_kernel(MeanCorrLaunch a, int nb, int ntiles) {
-  const int J = blockIdx.x, g = blockIdx.y;
+// First tile image of sequence s: sum over the sequences before it of ceil(nb / 32)
+// (every lane strides the sequences, then a butterfly sum, as seq_pos does).
+__device__ inline int64_t tile_base(const SeqDesc& sd, int s) {
+  if (sd.cu_seqlens == nullptr) return 0;
+  int64_t acc = 0;
+  for (int r = (int)(threadIdx.x & 63); r < s; r += 64) {
+    int n = sd.cu_seqlens[r + 1] - sd.cu_seqlens[r];
+    n = n < 0 ? 0 : n;
+    const int nb = (n + kBlock - 1) / kBlock;
+    acc += (nb + kTile - 1) / kTile;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  return uniform64(acc);
+}
+
+__global__ __launch_bounds__(kThreads) void meanprep_kernel(MeanCorrLaunch a) {
+  const int J = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
   const int tid = threadIdx.x;
+  const SeqPos sp = seq_pos(a.sd, s);
+  const int nb = (sp.len + kBlock - 1) / kBlock;
+  if (kTile * J >= nb) return;
   const int nk = min(kTile, nb - kTile * J);
-  unsigned char* img = (unsigned char*)a.workspace + ((int64_t)g * ntiles + J) * kTileBytes;
-  const double* kbar = a.pooled_k + ((int64_t)g * nb + kTile * J) * kHeadDim;
-  const double* vbar = a.pooled_v + ((int64_t)g * nb + kTile * J) * kHeadDim;
+  unsigned char* img = (unsigned char*)a.workspace + ((int64_t)g * a.total_tiles + tile_base(a.sd, s) + J) * kTileBytes;
+  const double* kbar = a.pooled_k + ((int64_t)g * a.sd.total_blocks + sp.blk0 + kTile * J) * kHeadDim;
+  const double* vbar = a.pooled_v + ((int64_t)g * a.sd.total_blocks + sp.blk0 + kTile * J) * kHeadDim;
   {  // Kbar row kr, dims 16dc .. +15 -> hi/lo (rows past nb are zero)
     const int kr = tid >> 3, dc = tid & 7;
     const f64x2* src = (const f64x2*)(kbar + kr * kHeadDim + 16 * dc);
@@ -111,23 +130,22 @@ __global__ __launch_bounds__(kThreads) void meanprep_kernel(MeanCorrLaunch a, in
   }
 }
 
-struct MCK {
-  MeanCorrLaunch a;
-  int nb, ntiles;
-};
-
-__global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MCK p) {
-  const MeanCorrLaunch& a = p.a;
+__global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MeanCorrLaunch a) {
   const int id = blockIdx.x;
   const int h = id % a.hq;
-  const int i = p.nb - 1 - id / a.hq;  // longest rows first
-  if (i <= 0) return;                  // block 0 has nothing below the diagonal
+  const int rest = id / a.hq;
+  const int s = rest % a.sd.n_seqs;
+  const int i = a.sd.max_nb - 1 - rest / a.sd.n_seqs;  // longest rows first
+  if (i <= 0) return;                                  // block 0 has nothing below the diagonal
+  const SeqPos sp = seq_pos(a.sd, s);
+  if (i * kBlock >= sp.len) return;
   const int g = h / (a.hq / a.hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const int64_t t = (int64_t)i * kBlock + 32 * w + ql;  // this lane's query
-  const bool valid = t < a.L;
+  const int64_t tl = (int64_t)i * kBlock + 32 * w + ql;  // this lane's query within the sequence
+  const bool valid = tl < sp.len;
+  const int64_t t = sp.tok0 + tl;                          // ... and in the packed batch
   const int nw = (i + kTile - 1) / kTile;  // tiles of keys j < i
 
   extern __shared__ unsigned listed[];  // nw words
@@ -137,9 +155,9 @@ __global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MCK p) {
   // ---- listed blocks of (h, i) as a bit mask
   for (int u = tid; u < nw; u += kThreads) listed[u] = 0u;
   __syncthreads();
-  int cnt = ((cint_ptr)a.counts)[(int64_t)h * p.nb + i];
+  int cnt = ((cint_ptr)a.counts)[(int64_t)h * a.sd.total_blocks + sp.blk0 + i];
   cnt = cnt < 0 ? 0 : (cnt > i + 1 ? i + 1 : cnt);
-  const int32_t* list = a.idx + (int64_t)h * ((int64_t)p.nb * (p.nb + 1) / 2) + (int64_t)i * (i + 1) / 2;
+  const int32_t* list = a.idx + (int64_t)h * a.sd.total_tri + sp.tri0 + (int64_t)i * (i + 1) / 2;
   for (int e = tid; e < cnt; e += kThreads) {
     const int j = list[e];
     if (j >= 0 && j < i) atomicOr(&listed[j >> 5], 1u << (j & 31));
@@ -159,8 +177,10 @@ __global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MCK p) {
   if (first < 0) return;  // nothing pruned: output and LSE stay bit-identical
 
   // ---- direct loads of a tile image: load u of wave w fills KB 4u + w
+  const int ntiles = ((sp.len + kBlock - 1) / kBlock + kTile - 1) / kTile;  // this sequence's tile images
   const __amdgpu_buffer_rsrc_t rws =
-      rsrc((const unsigned char*)a.workspace + (int64_t)g * p.ntiles * kTileBytes, (unsigned)(p.ntiles * kTileBytes));
+      rsrc((const unsigned char*)a.workspace + ((int64_t)g * a.total_tiles + tile_base(a.sd, s)) * kTileBytes,
+           (unsigned)(ntiles * kTileBytes));
   auto load_tile = [&](int J, unsigned char* buf) {
 #pragma unroll
     for (int u = 0; u < kTileBytes / 4096; ++u)
@@ -206,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MCK p) {
   f32x16 o[4];
   unsigned char* orow = (unsigned char*)a.out + (t * a.o_st + (int64_t)h * a.o_sh) * 2;
   if (valid) {
-    m = a.lse[(int64_t)h * a.L + t] * kLog2e;
+    m = a.lse[(int64_t)h * a.sd.total_tokens + t] * kLog2e;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -305,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void meancorr_kernel(MCK p) {
       for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[dt][4 * r + e] * inv);
       *(u32x2*)(orow + (32 * dt + 8 * r + 4 * hh) * 2) = __builtin_bit_cast(u32x2, ov);
     }
-  if (hh == 0) a.lse[(int64_t)h * a.L + t] = (m + __builtin_log2f(lt)) * kLn2;
+  if (hh == 0) a.lse[(int64_t)h * a.sd.total_tokens + t] = (m + __builtin_log2f(lt)) * kLn2;
 }
 
 }  // namespace
@@ -341,18 +361,25 @@ hipError_t meancorr_scratch(void** ptr) {
 
 int meancorr_max_blocks() { return kMaxBlocks; }
 
-int64_t meancorr_workspace_bytes(int L, int hkv) {
+int64_t meancorr_tile_bytes() { return kTileBytes; }
+
+int64_t meancorr_tiles(int L) {
   const int64_t nb = ((int64_t)L + kBlock - 1) / kBlock;
-  return (int64_t)hkv * ((nb + kTile - 1) / kTile) * kTileBytes;
+  return (nb + kTile - 1) / kTile;
 }
 
+// sum_s ceil(nb_s / 32) <= ceil(total_blocks / 32) + n_seqs
+int64_t meancorr_tiles_varlen(int64_t total_blocks, int n_seqs) { return (total_blocks + kTile - 1) / kTile + n_seqs; }
+
+int64_t meancorr_workspace_bytes(int L, int hkv) { return (int64_t)hkv * meancorr_tiles(L) * kTileBytes; }
+
 hipError_t launch_meancorr(const MeanCorrLaunch& a, hipStream_t st) {
-  const int nb = (int)((a.L + kBlock - 1) / kBlock);
-  const int ntiles = (nb + kTile - 1) / kTile;
-  hipLaunchKernelGGL(meanprep_kernel, dim3(ntiles, a.hkv), dim3(kThreads), 0, st, a, nb, ntiles);
-  MCK p{a, nb, ntiles};
-  const size_t mask_bytes = (size_t)ntiles * 4;
-  hipLaunchKernelGGL(meancorr_kernel, dim3((unsigned)((int64_t)a.hq * nb)), dim3(kThreads), mask_bytes, st, p);
+  const int max_tiles = (a.sd.max_nb + kTile - 1) / kTile;
+  if (max_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(meanprep_kernel, dim3(max_tiles, a.sd.n_seqs, a.hkv), dim3(kThreads), 0, st, a);
+  const size_t mask_bytes = (size_t)max_tiles * 4;
+  hipLaunchKernelGGL(meancorr_kernel, dim3((unsigned)((int64_t)a.hq * a.sd.max_nb * a.sd.n_seqs)), dim3(kThreads),
+                     mask_bytes, st, a);
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ enum fp_dtype {
 const char* fp_status_string(int status);
 /* Description of the last error returned on this host thread ("" if none). */
 const char* fp_last_error(void);
-/* Library ABI version (increments on any signature change; this header: 3). */
+/* Library ABI version (increments on any signature change; this header: 4). */
 int fp_abi_version(void);
 
 /* Host helpers: number of blocks ceil(L / block), and the idx capacity in
@@ -251,6 +251,53 @@ int fp_mean_correct(const void* q, int dtype, const float* q_scale,
 /* Workspace bytes fp_mean_correct needs for L tokens and hkv KV heads
  * (-1 for L < 0 or hkv < 1).  Host only. */
 int64_t fp_mean_correct_workspace_bytes(int L, int hkv);
+
+/* ---------------------------------------------------------------------------
+ * fp_mean_correct_varlen -- fp_mean_correct over a packed batch (the serving
+ * workload of the FlashPrefill V2 abstract: paged KV cache, continuous
+ * batching), applied to every sequence on its own.  Same assumption, off unless
+ * called.
+ *   q          packed [total_tokens, hq, d]; sequence s owns tokens
+ *              cu_seqlens[s] .. cu_seqlens[s+1]-1 (device int32 [n_seqs+1])
+ *   pooled_k/v [hkv, total_blocks, d] fp64, sequence s's blocks starting at
+ *              sum_{r<s} ceil(len_r/128) (as fp_discover_paged / fp_pool_varlen
+ *              write them)
+ *   idx/counts the lists of fp_threshold_compact_varlen
+ *   out, lse   packed [total_tokens, hq, d] / [hq, total_tokens], in place
+ *   workspace  fp_mean_correct_varlen_workspace_bytes(total_blocks, n_seqs, hkv)
+ *              bytes, 16-byte aligned (NULL, misaligned or short: FP_EINVAL)
+ * Sequences of at most 65536 blocks.  Other arguments and errors as
+ * fp_mean_correct and fp_sparse_attn_paged.
+ * ------------------------------------------------------------------------- */
+int fp_mean_correct_varlen(const void* q, int dtype, const float* q_scale,
+                           const double* pooled_k, const double* pooled_v,
+                           const int32_t* cu_seqlens, int n_seqs, int max_seqlen,
+                           int64_t total_tokens, int64_t total_blocks, int64_t total_tri,
+                           int hq, int hkv, int d, int block,
+                           int64_t q_stride_tok, int64_t q_stride_head,
+                           int64_t o_stride_tok, int64_t o_stride_head,
+                           const int32_t* idx, const int32_t* counts, float softmax_scale,
+                           void* out, float* lse, void* workspace, int64_t workspace_bytes,
+                           void* stream);
+
+/* Workspace bytes fp_mean_correct_varlen needs (an upper bound: hkv tile images of
+ * 24 KB per 32 blocks of every sequence, i.e. hkv * (ceil(total_blocks/32) +
+ * n_seqs) * 24576); -1 for negative sizes.  Host only. */
+int64_t fp_mean_correct_varlen_workspace_bytes(int64_t total_blocks, int n_seqs, int hkv);
+
+/* fp_pool over a packed batch: per-sequence block means of x, packed
+ * [total_tokens, H, d] (page_table NULL) or a page cache [num_pages, 128, H, d]
+ * through page_table [n_seqs, max_pages] -> pooled [H, total_blocks, d] fp64
+ * (sequence s's blocks starting at sum_{r<s} ceil(len_r/128); a partial last
+ * block is averaged over its valid rows).  Used to pool V for
+ * fp_mean_correct_varlen.  Arguments and errors as fp_discover_paged. */
+int fp_pool_varlen(const void* x, int dtype, const float* scale,
+                   const int32_t* cu_seqlens, int n_seqs, int max_seqlen,
+                   int64_t total_tokens, int64_t total_blocks,
+                   const int32_t* page_table, int max_pages, int num_pages,
+                   int H, int d, int block,
+                   int64_t stride_page, int64_t stride_tok, int64_t stride_head,
+                   double* pooled, void* stream);
 
 /* ---------------------------------------------------------------------------
  * fp_mean_correct_noalloc -- fp_mean_correct for callers that cannot allocate

@@ -245,6 +245,32 @@ def test_mean_correct_noalloc_rejects():
     assert lib.fp_mean_correct_noalloc(*empty) == _lib.FP_OK
 
 
+def test_mean_correct_varlen_and_pool_varlen_reject():
+    lib = _lib.load()
+    assert lib.fp_mean_correct_varlen_workspace_bytes(100, 3, 2) == 2 * (4 + 3) * 3 * 32 * 256
+    assert lib.fp_mean_correct_varlen_workspace_bytes(-1, 3, 2) == -1
+    assert lib.fp_mean_correct_varlen_workspace_bytes(10, 0, 2) == -1
+    ws = lib.fp_mean_correct_varlen_workspace_bytes(20, 2, 2)
+    args = [P, 0, None, P, P, P, 2, 1300, 2000, 20, 200, 4, 2, 128, 128, 512, 128, 512, 128, P, P, 0.088,
+            P, P, P, ws, None]
+    short = list(args); short[25] = ws - 1
+    assert lib.fp_mean_correct_varlen(*short) == EINVAL and b"workspace" in lib.fp_last_error()
+    no_cu = list(args); no_cu[5] = None
+    assert lib.fp_mean_correct_varlen(*no_cu) == EINVAL
+    no_lse = list(args); no_lse[23] = None
+    assert lib.fp_mean_correct_varlen(*no_lse) == EINVAL
+    empty = list(args); empty[8] = 0
+    assert lib.fp_mean_correct_varlen(*empty) == _lib.FP_OK
+    pargs = [P, 0, None, P, 2, 1300, 2000, 20, None, 0, 0, 2, 128, 128, 0, 256, 128, P, None]
+    assert lib.fp_pool_varlen(*pargs[:17], None, None) == EINVAL  # no output
+    bad = list(pargs); bad[3] = None
+    assert lib.fp_pool_varlen(*bad) == EINVAL
+    bad = list(pargs); bad[1] = 1  # fp8 without a scale
+    assert lib.fp_pool_varlen(*bad) == EINVAL
+    paged = list(pargs); paged[8] = P; paged[9] = 5; paged[10] = 8  # max_pages 5 < 11 blocks
+    assert lib.fp_pool_varlen(*paged) == EINVAL and b"max_pages" in lib.fp_last_error()
+
+
 def test_empty_inputs_are_a_no_op():
     """L = 0 validates and returns FP_OK without launching anything."""
     assert discover(L=0) == _lib.FP_OK

@@ -1,7 +1,7 @@
 """Guard zones around every output buffer: no entry point writes outside its extent.
 
 Each output (pooled means, idx, counts, score map, block mask, attention output,
-LSE, mean-correction workspace) is carved out of a larger allocation whose leading
+LSE, mean-correction workspace, single sequence and packed batch) is carved out of a larger allocation whose leading
 and trailing guard zones hold a fixed byte pattern.  After the calls the guards
 must still hold that pattern, for single-sequence, fp8, packed-batch (packed and
 paged K/V) and chunked-prefill runs.
@@ -113,6 +113,10 @@ def test_packed_batch_outputs_stay_in_bounds(paged):
         "out": Guarded((batch.total_tokens, hq, d), torch.bfloat16),
         "lse": Guarded((hq, batch.total_tokens), torch.float32),
         "dense_out": Guarded((batch.total_tokens, hq, d), torch.bfloat16),
+        "pooled_v": Guarded((hkv, batch.total_blocks, d), torch.float64),
+        "mc_workspace": Guarded((int(fp.load().fp_mean_correct_varlen_workspace_bytes(batch.total_blocks,
+                                                                                       batch.n_seqs, hkv)),),
+                                torch.uint8),
     }
     fp.discover_paged(q, kk, batch, page_table=pt, pooled_q=b["pooled_q"].t, pooled_k=b["pooled_k"].t)
     fp.threshold_compact_varlen(b["pooled_q"].t, b["pooled_k"].t, batch, 0.1, wl.n_sink, wl.n_local,
@@ -120,6 +124,9 @@ def test_packed_batch_outputs_stay_in_bounds(paged):
     fp.sparse_attn_paged(q, kk, vv, batch, b["idx"].t, b["counts"].t, page_table=pt, out=b["out"].t,
                          lse=b["lse"].t)
     fp.sparse_attn_paged(q, kk, vv, batch, page_table=pt, out=b["dense_out"].t)
+    fp.pool_varlen(vv, batch, page_table=pt, pooled=b["pooled_v"].t)
+    fp.mean_correct_varlen(q, b["pooled_k"].t, b["pooled_v"].t, batch, b["idx"].t, b["counts"].t, b["out"].t,
+                           b["lse"].t, workspace=b["mc_workspace"].t)
     assert_intact(b)
 
 

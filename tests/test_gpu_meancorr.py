@@ -84,3 +84,60 @@ def test_mean_correction_edge_lengths(L):
     assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 1e-3 * max(1.0, np.abs(ref_lse).max())
     # block 0 has nothing to correct: its rows are untouched
     assert torch.equal(out[:min(L, 128)], o0[:min(L, 128)]) and torch.equal(lse[:, :min(L, 128)], l0[:, :min(L, 128)])
+
+
+@pytest.mark.parametrize("dtype,paged", [("bf16", True), ("fp8", False)])
+def test_mean_correction_varlen_matches_definition_per_sequence(dtype, paged):
+    """Packed batch (ragged lengths, an empty and a single-block sequence): pooled V per
+    sequence is bit-exact (paged or packed V), and the corrected output and LSE of every
+    sequence match oracle.mean_correction on that sequence over the GPU's own lists."""
+    lengths = [128 * 23 + 77, 0, 100, 128 * 9, 128 * 40 + 3]
+    wl = synth.make_workload(f"mc_varlen_{dtype}", 8, 2, lengths, seed=47, dtype=dtype, paged=True,
+                             alphas=(0.2,), n_sink=1, n_local=3)
+    print(f"[case] mean correction varlen {dtype} paged={paged} lengths={lengths}", flush=True)
+    q, k, v, qs, ks, vs = to_device(wl)
+    kc, vc, table = synth.device_pages(wl)
+    batch = fp.VarlenBatch(wl.lengths, q.device)
+    kk, vv, pt = (kc, vc, table) if paged else (k, v, None)
+    pq, pk = fp.discover_paged(q, kk, batch, page_table=pt, q_scale=qs, k_scale=ks)
+    pv = fp.pool_varlen(vv, batch, page_table=pt, scale=vs)
+    idx, counts = fp.threshold_compact_varlen(pq, pk, batch, 0.2, wl.n_sink, wl.n_local)
+    out, lse = fp.sparse_attn_paged(q, kk, vv, batch, idx, counts, page_table=pt, q_scale=qs, k_scale=ks,
+                                    v_scale=vs, return_lse=True)
+    fp.mean_correct_varlen(q, pk, pv, batch, idx, counts, out, lse, q_scale=qs)
+    torch.cuda.synchronize()
+    oq, ok_, ov = oracle_inputs(wl)
+    idx_np, cnt_np = idx.cpu().numpy(), counts.cpu().numpy()
+    pv_np, out_np, lse_np = pv.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_FP8
+    cu = wl.cu_seqlens
+    for s in range(wl.n_seqs):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            continue
+        b0, b1 = batch.cu_blocks[s], batch.cu_blocks[s + 1]
+        assert np.array_equal(pv_np[:, b0:b1], O.pool(ov[a:b], 128)), s
+        lists = [unpack_lists(idx_np, cnt_np, h, b1 - b0, batch.total_tri, batch.cu_tri[s], b0) for h in range(wl.hq)]
+        ref, ref_lse = O.mean_correction(oq[a:b], ok_[a:b], ov[a:b], lists, 128, want_lse=True)
+        assert np.max(np.abs(out_np[a:b] - ref)) <= tol, s
+        assert np.max(np.abs(lse_np[:, a:b] - ref_lse)) <= 1e-3 * max(1.0, np.abs(ref_lse).max()), s
+
+
+def test_mean_correction_varlen_single_sequence_equals_contiguous():
+    """A one-sequence batch gives bit for bit what the single-sequence call gives."""
+    wl = workload("gqa_ragged")
+    print(f"[case] mean correction varlen == single L={wl.L}", flush=True)
+    q, k, v, *_ = to_device(wl)
+    batch = fp.VarlenBatch([wl.L], q.device)
+    pq, pk = fp.discover(q, k)
+    pv = fp.pool(v)
+    assert torch.equal(fp.pool_varlen(v, batch), pv)
+    idx, counts = fp.threshold_compact(pq, pk, 0.3, wl.n_sink, wl.n_local)
+    out, lse = fp.sparse_attn(q, k, v, idx, counts, return_lse=True)
+    o1, l1 = out.clone(), lse.clone()
+    o2, l2 = out.clone(), lse.clone()
+    fp.mean_correct(q, pk, pv, idx, counts, o1, l1)
+    fp.mean_correct_varlen(q, pk, pv, batch, idx, counts, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert not torch.equal(o1, out)
