@@ -684,7 +684,7 @@ def main():
         torch.cuda.empty_cache()
         wl8 = synth.make_config(3)
         f8 = workload_line(wl8, wl8.alphas[0], max(2, args.steps // 2), 1, peaks, dense=not args.no_dense)
-        f8["roofline"]["traffic"] = counter_traffic("attn_256k_fp8_hbm_traffic.txt")
+        f8["roofline"]["traffic"] = counter_traffic("attn_256k_fp8_counters.txt")
         extra["fp8_256k"] = f8
         del wl8
         log(f"fp8 256K step {f8['ms_per_step']:.2f} ms, attention {f8['roofline']['frac'] * 100:.1f}% of fp8 peak")
@@ -729,7 +729,7 @@ def main():
                    "alpha": alpha, "n_sink": wl.n_sink, "n_local": wl.n_local, "batch": 1,
                    "step": "discover + threshold_compact + sparse_attn"},
         "roofline": roofline_block(f"attn_kernel (sparse, {wl.dtype})", computed_flops, r["attn_ms"], wl.dtype, peaks,
-                                   counter_traffic("attn_128k_bf16_hbm_traffic.txt") if args.config == 2 else None),
+                                   counter_traffic("attn_128k_bf16_counters.txt") if args.config == 2 else None),
         "extra": extra,
     }
     if args.calibrate:
