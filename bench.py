@@ -454,15 +454,26 @@ def measured_peaks():
 
 
 def roofline_block(kernel, computed_flops, ms, dtype, peaks, traffic=None):
+    """MFMA roofline of a sparse attention launch (computed flops over its time, against
+    the datasheet and the measured matrix-core peak).  With the counter traffic of the
+    launch (profiles/), also the rate at which that traffic moves beyond L2, against the
+    HBM datasheet peak and the measured streaming-read peak."""
     peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP8_TFLOPS
     achieved = computed_flops / (ms * 1e-3) / 1e12
     meas = peaks.get("mfma_bf16_tflops" if dtype == "bf16" else "mfma_fp8_tflops") if peaks else None
-    return {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": traffic,
-            "peak_measured": meas, "frac_measured": (achieved / meas) if meas else None}
+    block = {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+             "frac": achieved / peak, "traffic": traffic,
+             "peak_measured": meas, "frac_measured": (achieved / meas) if meas else None}
+    if traffic:
+        rate = traffic / (ms * 1e-3) / 1e9
+        block["traffic_gbs"] = rate
+        block["traffic_frac_hbm_peak"] = rate / PEAK_HBM_GBS
+        if peaks:
+            block["traffic_frac_stream_measured"] = rate / peaks["stream_read_gbs"]
+    return block
 
 
-def workload_line(wl, alpha, steps, warmup, peaks, dense=True):
+def workload_line(wl, alpha, steps, warmup, peaks, dense=True, traffic=None):
     """One workload's hot path (per-stage HIP events) beside the same-GPU dense kernel."""
     import torch
     r = time_hot_path(wl, steps, warmup, alpha)
@@ -475,7 +486,8 @@ def workload_line(wl, alpha, steps, warmup, peaks, dense=True):
         "stage_ms": dict(zip(("discover", "threshold_compact", "sparse_attn"), r["stage_median"])),
         "ms_per_step": r["ms_per_step"],
         "dense_equiv_tflops": dense_eq / (r["ms_per_step"] * 1e-3) / 1e12,
-        "roofline": roofline_block(f"attn_kernel (sparse, {wl.dtype})", comp, r["stage_median"][2], wl.dtype, peaks),
+        "roofline": roofline_block(f"attn_kernel (sparse, {wl.dtype})", comp, r["stage_median"][2], wl.dtype, peaks,
+                                   traffic),
     }
     if dense:
         dms = time_dense(r["tensors"], reps=1 if L > 131072 else 2)
@@ -683,8 +695,9 @@ def main():
             f"attention {pb['paged']['mfma_frac'] * 100:.1f}% of MFMA peak")
         torch.cuda.empty_cache()
         wl8 = synth.make_config(3)
-        f8 = workload_line(wl8, wl8.alphas[0], max(2, args.steps // 2), 1, peaks, dense=not args.no_dense)
-        f8["roofline"]["traffic"] = counter_traffic("attn_256k_fp8_counters.txt")
+        f8 = workload_line(wl8, wl8.alphas[0], max(2, args.steps // 2), 1, peaks, dense=not args.no_dense,
+                           traffic=counter_traffic("attn_256k_fp8_counters.txt"))
+
         extra["fp8_256k"] = f8
         del wl8
         log(f"fp8 256K step {f8['ms_per_step']:.2f} ms, attention {f8['roofline']['frac'] * 100:.1f}% of fp8 peak")
