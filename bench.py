@@ -447,9 +447,21 @@ def measured_peaks():
     ms = timed(lambda: lib.fpk_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), cus * 8,
                                            ctypes.c_void_p(word.data_ptr()), ctypes.c_void_p(st)))
     res["stream_read_gbs"] = buf.numel() / (ms * 1e-3) / 1e9
+    # ordinary loads over one working set, 8 GiB in total per launch: L2-resident (2 MB per
+    # XCD), Infinity-Cache-resident, and HBM
+    lib.fpk_read_passes.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    by_size = {}
+    for label, size in (("16MB_l2", 16 << 20), ("128MB_infinity_cache", 128 << 20), ("4GB_hbm", 4 << 30)):
+        passes = (8 << 30) // size
+        ms = timed(lambda: lib.fpk_read_passes(ctypes.c_void_p(buf.data_ptr()), size, passes, cus * 8,
+                                               ctypes.c_void_p(word.data_ptr()), ctypes.c_void_p(st)), reps=3)
+        by_size[label] = size * passes / (ms * 1e-3) / 1e9
+    res["read_gbs_by_working_set"] = by_size
     del buf
     res["note"] = ("one 4-wave workgroup per CU of back-to-back independent 32x32 products on register "
-                   "operands; 16-byte non-temporal loads over 4 GiB")
+                   "operands; 16-byte non-temporal loads over 4 GiB; ordinary loads over 16 MB / 128 MB / 4 GiB "
+                   "working sets")
     return res
 
 
@@ -614,7 +626,8 @@ def main():
     try:
         peaks = measured_peaks()
         log(f"measured peaks: bf16 MFMA loop {peaks['mfma_bf16_tflops']:.0f} TFLOP/s, fp8 "
-            f"{peaks['mfma_fp8_tflops']:.0f} TFLOP/s, streaming read {peaks['stream_read_gbs']:.0f} GB/s")
+            f"{peaks['mfma_fp8_tflops']:.0f} TFLOP/s, streaming read {peaks['stream_read_gbs']:.0f} GB/s; reads by "
+            "working set " + ", ".join(f"{k} {v:.0f} GB/s" for k, v in peaks["read_gbs_by_working_set"].items()))
     except OSError as e:  # the peaks library is optional: fractions then use the datasheet only
         log(f"no measured peaks ({e})")
 

@@ -8,7 +8,10 @@
 //                   instruction-issue ceiling of the matrix cores;
 //   fpk_stream_read 16-byte non-temporal loads over a buffer much larger than the
 //                   caches, summed so the loads cannot be dropped: the streaming HBM
-//                   read ceiling.
+//                   read ceiling;
+//   fpk_read_passes ordinary 16-byte loads over the same working set several times in
+//                   one launch: with a few MB per XCD it measures L2 bandwidth, with
+//                   64-256 MB the Infinity Cache, beyond that HBM.
 // Both enqueue on the caller's stream and allocate nothing; the caller times them.
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -57,6 +60,18 @@ __global__ __launch_bounds__(256, 1) void mfma_loop_kernel(float* sink, int iter
   sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+__global__ __launch_bounds__(256) void read_passes_kernel(const u32x4* __restrict__ src, int64_t n16, int passes,
+                                                          unsigned* __restrict__ sink) {
+  unsigned acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int p = 0; p < passes; ++p)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+      const u32x4 x = src[i];
+      acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+    }
+  if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; practically never stores
+}
+
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                           unsigned* __restrict__ sink) {
   unsigned acc = 0;
@@ -95,6 +110,17 @@ int fpk_stream_read(const void* src, int64_t bytes, int workgroups, unsigned* si
     return 1;
   hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4*)src, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// Reads `bytes` (a multiple of 16) from src `passes` times in one launch; sink: one
+// device word.
+int fpk_read_passes(const void* src, int64_t bytes, int passes, int workgroups, unsigned* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || bytes <= 0 || (bytes & 15) || ((uintptr_t)src & 15) || workgroups < 1 ||
+      passes < 1)
+    return 1;
+  hipLaunchKernelGGL(read_passes_kernel, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)src, bytes / 16, passes, sink);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
