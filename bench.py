@@ -718,7 +718,8 @@ def main():
     if not args.no_configs and args.config == 2:
         import torch
         # the other workloads, each beside the same-GPU dense kernel: the 4K config,
-        # the 32K config at its three alphas, and the 128K workload quantised to fp8
+        # the 32K config at its three alphas, the 128K workload quantised to fp8, and the
+        # structured extra
         lines = {}
         wl0 = synth.make_config(0)
         lines["tiny_4k"] = workload_line(wl0, wl0.alphas[0], args.steps, args.warmup, peaks, dense=not args.no_dense)
@@ -731,6 +732,13 @@ def main():
         lines["fp8_128k"] = workload_line(wlf, wlf.alphas[0], max(2, args.steps // 2), 1, peaks,
                                           dense=not args.no_dense)
         del wlf
+        torch.cuda.empty_cache()
+        # an extra, labelled workload (not one of the five configurations): the 128K shapes
+        # with structured patterns shared within KV groups, ~3.6% of causal blocks kept
+        wls = synth.make_structured()
+        lines["structured_128k_extra"] = workload_line(wls, wls.alphas[0], args.steps, args.warmup, peaks,
+                                                       dense=not args.no_dense)
+        del wls
         torch.cuda.empty_cache()
         for name, ln in lines.items():
             log(f"{name}: step {ln['ms_per_step']:.3f} ms, density {ln['density']:.3f}, attention "

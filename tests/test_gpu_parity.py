@@ -40,6 +40,8 @@ def workload(name):
         return synth.make_workload(name, 2, 2, [100], seed=23, alphas=(0.1,), n_sink=1, n_local=1)
     if name == "gqa7":  # Qwen2.5-7B head ratio (28/4 -> 7), short
         return synth.make_workload(name, 7, 1, [128 * 20 + 1], seed=24, alphas=(0.2,), n_sink=2, n_local=2)
+    if name == "structured":  # the sparser structured recipe: peaked rows, heads sharing blocks
+        return synth.make_structured(L=128 * 90 + 57, hq=8, hkv=2, seed=25)
     raise KeyError(name)
 
 
@@ -50,7 +52,7 @@ def oracle_selection(name, alpha):
     return O.select_blocks(q, k, 128, alpha, wl.n_sink, wl.n_local)
 
 
-CASES = ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block", "gqa7"]
+CASES = ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block", "gqa7", "structured"]
 
 
 def run_gpu(wl, alpha):

@@ -62,3 +62,33 @@ def test_config_shapes():
     assert synth.config_lengths(2) == [131072]
     wl = synth.make_config(0)
     assert wl.q.shape == (4096, 1, 128) and wl.n_local == 2 and wl.alphas == (0.1,)
+
+
+def test_structured_recipe_is_sparser_and_shared_within_groups():
+    # same size and heads, standard recipe vs the structured one: far fewer kept blocks,
+    # and the heads of a KV group keep largely the same blocks
+    L, hq, hkv = 128 * 128, 8, 1
+    std = synth.make_workload("std", hq, hkv, [L], seed=9)
+    st = synth.make_structured(L=L, hq=hq, hkv=hkv, seed=9)
+    dens, lift = {}, {}
+    for tag, wl in (("std", std), ("structured", st)):
+        q = O.decode_bf16(wl.q).astype(np.float64)
+        k = O.decode_bf16(wl.k).astype(np.float64)
+        keep = O.select_blocks(q, k, 128, 0.1, 1, 4)["keep"].reshape(hq, -1)
+        nb = int(round(np.sqrt(keep.shape[1])))
+        dens[tag] = keep.sum() / (hq * nb * (nb + 1) / 2)
+        # chance that a block one head keeps is kept by another head of the group, over the
+        # density (1 for independent heads)
+        both = sum((keep[a] & keep[b]).sum() for a in range(hq) for b in range(hq) if a != b)
+        lift[tag] = both / ((hq - 1) * keep.sum()) / dens[tag]
+    assert dens["structured"] < 0.5 * dens["std"]
+    assert lift["structured"] > 2.0 * lift["std"]
+
+
+def test_default_knobs_leave_the_standard_recipe_unchanged():
+    a = synth.make_workload("a", 2, 1, [900], seed=11, d=32, block=64)
+    b = synth.make_workload("a", 2, 1, [900], seed=11, d=32, block=64, mean_scale=1.0,
+                            vertical_gain=synth.VERTICAL_GAIN, slash_period=synth.SLASH_PERIOD_BLOCKS)
+    assert a.digests() == b.digests()
+    c = synth.make_workload("a", 2, 1, [900], seed=11, d=32, block=64, mean_scale=0.5)
+    assert c.digests()["q"] != a.digests()["q"]
