@@ -485,8 +485,9 @@ def roofline_block(kernel, computed_flops, ms, dtype, peaks, traffic=None):
     return block
 
 
-def workload_line(wl, alpha, steps, warmup, peaks, dense=True, traffic=None):
-    """One workload's hot path (per-stage HIP events) beside the same-GPU dense kernel."""
+def workload_line(wl, alpha, steps, warmup, peaks, dense=True, traffic=None, grouped=False):
+    """One workload's hot path (per-stage HIP events) beside the same-GPU dense kernel
+    (and, with grouped, the group-shared-lists variant on the same inputs)."""
     import torch
     r = time_hot_path(wl, steps, warmup, alpha)
     nb, hq, d, L = r["nb"], wl.hq, wl.d, wl.L
@@ -501,6 +502,8 @@ def workload_line(wl, alpha, steps, warmup, peaks, dense=True, traffic=None):
         "roofline": roofline_block(f"attn_kernel (sparse, {wl.dtype})", comp, r["stage_median"][2], wl.dtype, peaks,
                                    traffic),
     }
+    if grouped:
+        line["group_shared_lists"] = time_grouped(r, wl, alpha)
     if dense:
         dms = time_dense(r["tensors"], reps=1 if L > 131072 else 2)
         line["dense_attn_ms"] = dms
@@ -737,7 +740,7 @@ def main():
         # with structured patterns shared within KV groups, ~3.6% of causal blocks kept
         wls = synth.make_structured()
         lines["structured_128k_extra"] = workload_line(wls, wls.alphas[0], args.steps, args.warmup, peaks,
-                                                       dense=not args.no_dense)
+                                                       dense=not args.no_dense, grouped=True)
         del wls
         torch.cuda.empty_cache()
         for name, ln in lines.items():
