@@ -111,17 +111,26 @@ __global__ __launch_bounds__(kThreads, (DT == 0 || LSE) ? 2 : 3) void attn_kerne
 
   const AttnLaunch& a = p.a;
   // Work decode: query heads fastest so that consecutive workgroups share the
-  // same query block; with hq % 8 == 0 each XCD (workgroup id % 8) receives a
-  // contiguous run of heads, i.e. heads of one KV group, for L2 reuse of K/V.
+  // same query block, heaviest query blocks first.  Workgroup id % 8 is the XCD
+  // (each with its own L2), so the heads an XCD receives should share K/V: with
+  // hq % 8 == 0 each XCD takes a contiguous run of hq/8 heads (heads of one KV
+  // group); otherwise, when the KV heads divide 8, each group goes to 8/hkv XCDs
+  // that split its rows (else heads are dealt round robin).
   const int id = blockIdx.x;
-  int h;
+  const int rows = p.sd.max_nq * p.sd.n_seqs;  // workgroups per query head
+  int h, rest;
   if ((a.hq & 7) == 0) {
     const int per = a.hq >> 3;
     h = (id & 7) * per + ((id >> 3) % per);
+    rest = id / a.hq;
+  } else if (8 % a.hkv == 0 && rows % (8 / a.hkv) == 0) {
+    const int xg = 8 / a.hkv, x = id & 7, k = id >> 3;
+    h = (x / xg) * p.group + k % p.group;
+    rest = (k / p.group) * xg + x % xg;
   } else {
     h = id % a.hq;
+    rest = id / a.hq;
   }
-  const int rest = id / a.hq;
   const int s = rest % p.sd.n_seqs;
   const int r = p.sd.max_nq - 1 - rest / p.sd.n_seqs;  // heaviest query blocks first
   SeqPos sp = seq_pos(p.sd, s);
