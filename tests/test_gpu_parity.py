@@ -42,6 +42,8 @@ def workload(name):
         return synth.make_workload(name, 7, 1, [128 * 20 + 1], seed=24, alphas=(0.2,), n_sink=2, n_local=2)
     if name == "structured":  # the sparser structured recipe: peaked rows, heads sharing blocks
         return synth.make_structured(L=128 * 90 + 57, hq=8, hkv=2, seed=25)
+    if name == "gqa28x4_short":  # hq not a multiple of 8: KV groups on XCD pairs (10 query blocks)
+        return synth.make_workload(name, 28, 4, [128 * 9 + 17], seed=26, alphas=(0.2,), n_sink=1, n_local=2)
     raise KeyError(name)
 
 
@@ -52,7 +54,7 @@ def oracle_selection(name, alpha):
     return O.select_blocks(q, k, 128, alpha, wl.n_sink, wl.n_local)
 
 
-CASES = ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block", "gqa7", "structured"]
+CASES = ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block", "gqa7", "structured", "gqa28x4_short"]
 
 
 def run_gpu(wl, alpha):
@@ -121,7 +123,7 @@ def test_scores_match_oracle(name):
     assert torch.equal(cnt0, cnt1) and torch.equal(idx0, idx1)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block"])
+@pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "fp8_ragged", "mha_one_block", "gqa28x4_short"])
 def test_dense_matches_oracle(name):
     wl = workload(name)
     print(f"[case] dense {name}", flush=True)
