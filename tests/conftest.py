@@ -9,3 +9,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: large host-side work (full-size workloads)")
+
+
+def pytest_terminal_summary(terminalreporter):
+    import helpers
+    if helpers.MARGINS:
+        terminalreporter.section("parity margins (worst error / bound)")
+        for line in helpers.MARGINS:
+            terminalreporter.write_line(line)

@@ -18,7 +18,8 @@ import torch
 import block_sparse_long_pooled_amd as fp
 import oracle as O
 import synth
-from helpers import TOL_BF16, TOL_FP8, check_lists, oracle_inputs, to_device, to_device_paged, unpack_lists
+from helpers import (TOL_BF16, TOL_FP8, check_lists, oracle_inputs, record_margin, to_device, to_device_paged,
+                     unpack_lists)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
@@ -98,8 +99,10 @@ def test_single_sequence_config(k):
         lse_np = lse.cpu().numpy()
         rows = stratified_rows(cnt_np, seed=100 + k)
         worst, worst_lse = check_rows(oq, ok_, ov, lists, out_np, lse_np, rows, tol, f"{wl.name} alpha={alpha}")
-        print(f"  alpha={alpha}: density {cnt_np.sum() / (wl.hq * tri):.4f}, in-band {n_amb}, "
-              f"{len(rows)} sampled rows: max-abs {worst:.3e} (bound {tol}), LSE {worst_lse:.3e}", flush=True)
+        msg = (f"{wl.name} alpha={alpha}: density {cnt_np.sum() / (wl.hq * tri):.4f}, in-band {n_amb}, "
+               f"{len(rows)} sampled rows: max-abs {worst:.3e} (bound {tol}), LSE {worst_lse:.3e}")
+        print("  " + msg, flush=True)
+        record_margin(msg)
 
 
 @pytest.mark.parametrize("k", [2, 3])
@@ -118,7 +121,9 @@ def test_dense_sampled_rows(k):
     full = [np.arange(i + 1) for i in range(nb)]
     rows = sorted({(h, i) for h in range(wl.hq) for i in (0, 1, nb - 1)} | set(sample_rows(wl.hq, nb, 4, seed=7)))
     worst, _ = check_rows(oq, ok_, ov, [full] * wl.hq, out_np, None, rows, tol, f"dense {wl.name}")
-    print(f"  dense {wl.name}: {len(rows)} sampled rows, max-abs {worst:.3e} (bound {tol})", flush=True)
+    msg = f"dense {wl.name}: {len(rows)} sampled rows, max-abs {worst:.3e} (bound {tol})"
+    print("  " + msg, flush=True)
+    record_margin(msg)
 
 
 def test_paged_batch_config():
@@ -152,5 +157,7 @@ def test_paged_batch_config():
         err, _ = check_rows(oq[a:b], ok_[a:b], ov[a:b], lists, out_np[a:b], None, rows, TOL_BF16,
                             f"paged batch sequence {s}")
         worst = max(worst, err)
-    print(f"  paged batch: {wl.n_seqs} sequences x {wl.hq} heads x first/last block, max-abs {worst:.3e} "
-          f"(bound {TOL_BF16})", flush=True)
+    msg = (f"paged batch: {wl.n_seqs} sequences x {wl.hq} heads x first/last block, max-abs {worst:.3e} "
+           f"(bound {TOL_BF16})")
+    print("  " + msg, flush=True)
+    record_margin(msg)

@@ -20,7 +20,7 @@ import torch
 import block_sparse_long_pooled_amd as fp
 import oracle as O
 import synth
-from helpers import (TOL_BF16, TOL_FP8, check_lists, oracle_inputs, to_device, to_device_paged,
+from helpers import (TOL_BF16, TOL_FP8, check_lists, oracle_inputs, record_margin, to_device, to_device_paged,
                      unpack_lists)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -94,7 +94,9 @@ def test_lists_and_attention_match_oracle(name):
         ref, ref_lse = O.sparse_attention(q, k, v, lists, 128, want_lse=True)
         err = np.max(np.abs(r["out"] - ref))
         tol = TOL_BF16 if wl.dtype == "bf16" else TOL_FP8
-        print(f"  max-abs err {err:.3e} (tol {tol}), density {r['counts'].sum() / (wl.hq * tri):.3f}", flush=True)
+        msg = f"{name} alpha={alpha}: full output max-abs {err:.3e} (bound {tol}), density {r['counts'].sum() / (wl.hq * tri):.3f}"
+        print("  " + msg, flush=True)
+        record_margin(msg)
         assert err <= tol
         assert np.max(np.abs(r["lse"] - ref_lse.astype(np.float32))) <= 1e-3 * max(1.0, np.abs(ref_lse).max())
 
